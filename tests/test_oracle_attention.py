@@ -1,0 +1,200 @@
+"""Pins for the oracle's phased mixed-precision attention (CPU)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import layout, draft, pipeline, attention, quant
+from video_dit_mixed_amd import synth
+
+
+def _small_case(T=2, H=7, W=9, D=32, rh=4, rw=4, seed=0, quota=(0, 0, 0, 10000), lam=0.5):
+    rng = np.random.default_rng(seed)
+    N = T * H * W
+    mk = lambda s: synth.f32_to_bf16_bits((rng.standard_normal((N, D)) * s).astype(np.float32))
+    q, k, v = mk(1.5), mk(1.5), mk(1.0)
+    return q, k, v, dict(T=T, H=H, W=W, rh=rh, rw=rw, lam=lam, quota_bp=quota)
+
+
+def _dense(q, k, v, D):
+    qf, kf, vf = (pipeline.bf16_bits_to_f64(a) for a in (q, k, v))
+    L = qf @ kf.T / np.sqrt(D)
+    P = np.exp(L - L.max(1, keepdims=True))
+    return (P @ vf) / P.sum(1, keepdims=True)
+
+
+def test_all_16bit_without_rounding_equals_dense_attention():
+    q, k, v, kw = _small_case()
+    r = pipeline.run_head(q, k, v, emulate_p_rounding=False, **kw)
+    out = layout.unpack(r.out_packed, r.g)
+    ref = _dense(q, k, v, 32)
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-12
+    qt, kt, vt = (torch.from_numpy(pipeline.bf16_bits_to_f64(a))[None, None] for a in (q, k, v))
+    sdpa = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0].numpy()
+    assert np.linalg.norm(out - sdpa) / np.linalg.norm(sdpa) <= 1e-12
+
+
+def test_all_16bit_with_p_rounding_close_to_dense():
+    q, k, v, kw = _small_case(seed=1)
+    r = pipeline.run_head(q, k, v, emulate_p_rounding=True, **kw)
+    out = layout.unpack(r.out_packed, r.g)
+    ref = _dense(q, k, v, 32)
+    assert np.linalg.norm(out - ref) / np.linalg.norm(ref) <= 2.0 ** -8
+
+
+def test_all_skip_gives_zero():
+    q, k, v, kw = _small_case(quota=(10000, 0, 0, 0))
+    r = pipeline.run_head(q, k, v, **kw)
+    assert np.all(r.out_packed[~np.isnan(r.out_packed)] == 0)
+    assert np.all(r.out_bf16() == 0)
+
+
+def _mixed_head(seed=2):
+    q, k, v, kw = _small_case(seed=seed, quota=(2000, 3000, 2500, 2500))
+    return q, k, v, kw, pipeline.prepare_head(q, k, v, **kw)
+
+
+def test_order_invariance_without_rounding():
+    q, k, v, kw, r = _mixed_head()
+    ops = pipeline._Ops(r)
+    rng = np.random.default_rng(9)
+    for qb in range(r.g.Nb):
+        _, O1, l1 = attention.attend_block(ops, qb, emulate_p_rounding=False)
+        perm = lambda kbs: rng.permutation(kbs)
+        _, O2, l2 = attention.attend_block(ops, qb, emulate_p_rounding=False,
+                                           phase_order=(1, 3, 2), kb_order=perm)
+        np.testing.assert_allclose(O1, O2, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(l1, l2, rtol=1e-12)
+
+
+def test_closed_form_masked_softmax_over_dequantised_scores():
+    """Rounding off: each query row equals softmax over all kept real keys, each key block scored
+    with its own level's dequantised operands, times that level's V."""
+    q, k, v, kw, r = _mixed_head(seed=3)
+    g, D, B = r.g, r.D, r.B
+    r2 = pipeline.attend(r, emulate_p_rounding=False)
+    s8 = np.sqrt(D)
+    for qb in range(g.Nb):
+        rows = qb * B + np.flatnonzero(r.valid[qb])
+        scores, vals = [], []
+        for kb in range(g.Nb):
+            lv = r.levels[qb, kb]
+            if lv == 0:
+                continue
+            ks = slice(kb * B, (kb + 1) * B)
+            keep = r.valid[kb]
+            if lv == 3:
+                S = r.qp[rows] @ r.kp[ks].T / s8
+                Vb = r.vp[ks]
+            elif lv == 2:
+                qd = r.q_i8[rows].astype(np.float64) * float(r.q_i8_s[qb])
+                kd = r.k_i8[ks].astype(np.float64) * float(r.k_i8_s[kb])
+                S = qd @ kd.T / s8
+                Vb = quant.e4m3fn_decode(r.v_fp8[ks]) * r.v_s.astype(np.float64)
+            else:
+                S = quant.mxfp4_decode(r.q_fp4[rows], r.q_e8[rows]) @ \
+                    quant.mxfp4_decode(r.k_fp4[ks], r.k_e8[ks]).T / s8
+                Vb = quant.e4m3fn_decode(r.v_fp8[ks]) * r.v_s.astype(np.float64)
+            scores.append(S[:, keep])
+            vals.append(Vb[keep])
+        if not scores:
+            assert np.all(r2.out_packed[rows] == 0)
+            continue
+        S = np.concatenate(scores, axis=1)
+        Vc = np.concatenate(vals, axis=0)
+        P = np.exp(S - S.max(1, keepdims=True))
+        ref = (P @ Vc) / P.sum(1, keepdims=True)
+        np.testing.assert_allclose(r2.out_packed[rows], ref, rtol=1e-11, atol=1e-13)
+
+
+def test_int8_scores_equal_exact_integer_dot_products():
+    q, k, v, kw, r = _mixed_head(seed=4)
+    ops = pipeline._Ops(r)
+    B, D = r.B, r.D
+    qb, kb = 1, 2
+    rows = qb * B + np.flatnonzero(r.valid[qb])
+    S = attention.block_scores(ops, draft.LEVEL_8, qb, kb, rows)
+    for i, row in enumerate(rows[:5]):
+        for j in range(B):
+            dot = sum(int(r.q_i8[row, d]) * int(r.k_i8[kb * B + j, d]) for d in range(D))
+            exp = float(dot) * float(r.q_i8_s[qb]) * float(r.k_i8_s[kb]) / np.sqrt(float(D))
+            assert S[i, j] == exp
+
+
+def test_fp8_p_rounding_uses_running_max_per_block():
+    """With rounding on, processing a row's blocks in another order changes the result, so the
+    per-block order is part of the definition (and is what the device must follow)."""
+    q, k, v, kw, r = _mixed_head(seed=5)
+    ops = pipeline._Ops(r)
+    diffs = []
+    for qb in range(r.g.Nb):
+        _, O1, _ = attention.attend_block(ops, qb, emulate_p_rounding=True)
+        _, O2, _ = attention.attend_block(ops, qb, emulate_p_rounding=True, kb_order=lambda x: x[::-1])
+        diffs.append(np.abs(O1 - O2).max())
+    assert max(diffs) > 0
+
+
+def test_pad_queries_and_keys_do_not_leak():
+    # A ragged grid: pad keys must get zero weight; changing nothing but pad handling is caught by
+    # comparing with dense attention over the real tokens only.
+    q, k, v, kw = _small_case(T=1, H=5, W=7, rh=4, rw=4, seed=6)
+    r = pipeline.run_head(q, k, v, emulate_p_rounding=False, **kw)
+    out = layout.unpack(r.out_packed, r.g)
+    ref = _dense(q, k, v, 32)
+    assert np.linalg.norm(out - ref) / np.linalg.norm(ref) <= 1e-12
+
+
+@pytest.mark.parametrize("level", [3, 2, 1])
+def test_single_block_p_rounding_matches_torch_casts(level):
+    """One kept block per row: O = round(P) V / sum(P) with round = bf16 (16-bit) or
+    e4m3(2^8 P) 2^-8 (low-bit), P = exp(S - rowmax); the casts here are PyTorch's."""
+    q, k, v, kw = _small_case(T=1, H=8, W=8, rh=4, rw=4, seed=7)
+    r = pipeline.prepare_head(q, k, v, **kw)
+    lv = np.zeros_like(r.levels)
+    for qb in range(r.g.Nb):
+        lv[qb, (qb + 1) % r.g.Nb] = level
+    r.levels_override = lv
+    pipeline.attend(r)
+    ops = pipeline._Ops(r)
+    B = r.B
+    for qb in range(r.g.Nb):
+        kb = (qb + 1) % r.g.Nb
+        rows = qb * B + np.flatnonzero(r.valid[qb])
+        S = attention.block_scores(ops, level, qb, kb, rows)
+        P = np.exp(S - S.max(1, keepdims=True))
+        Pt = torch.from_numpy(P)
+        ks = slice(kb * B, (kb + 1) * B)
+        if level == 3:
+            Pq = Pt.to(torch.bfloat16).to(torch.float64).numpy()
+            Vb = r.vp[ks]
+        else:
+            Pq = (Pt * 256).to(torch.float8_e4m3fn).to(torch.float64).numpy() / 256
+            Vb = torch.from_numpy(r.v_fp8[ks]).view(torch.float8_e4m3fn).to(torch.float64).numpy() \
+                * r.v_s.astype(np.float64)
+        ref = (Pq @ Vb) / P.sum(1, keepdims=True)
+        np.testing.assert_allclose(r.out_packed[rows], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_prepared_operands_dequantise_to_their_own_tensor():
+    """Every quantised operand of a prepared head decodes back to its own packed tensor within
+    its format's error bound (catches swapped tensors, blocks or channels)."""
+    w = synth.workload(1)
+    q, k, v = synth.make_head(w, 3)
+    r = pipeline.prepare_head(q, k, v, T=w.T, H=w.H, W=w.W, rh=w.region_h, rw=w.region_w,
+                              lam=w.lam, quota_bp=w.quota_bp)
+    B = r.B
+    for x, c, s in ((r.qp, r.q_i8, r.q_i8_s), (r.kp, r.k_i8, r.k_i8_s)):
+        for b in range(r.g.Nb):
+            blk = slice(b * B, (b + 1) * B)
+            sb = float(s[b])
+            assert sb == np.float32(np.abs(x[blk]).max()) / np.float32(127)
+            assert np.all(np.abs(x[blk] - c[blk] * sb) <= sb * (0.5 + 2.0 ** -14))
+    for x, c, e in ((r.qp, r.q_fp4, r.q_e8), (r.kp, r.k_fp4, r.k_e8)):
+        deq = quant.mxfp4_decode(c, e)
+        gmax = np.repeat(np.abs(x.reshape(-1, r.D // 32, 32)).max(axis=2), 32, axis=1)
+        assert np.all(np.abs(deq - x) <= gmax * 0.25 + 1e-300)   # half a step of 2^(e+1) <= amax/4
+    vreal = pipeline.bf16_bits_to_f64(v)
+    deq = r.v_fp8_val
+    amax = np.abs(vreal).max(axis=0)
+    big = np.abs(r.vp) >= amax * 2.0 ** -6
+    assert np.all(np.abs(deq - r.vp)[big] <= np.abs(r.vp)[big] * 2.0 ** -4 * 1.0001)
