@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header declares,
+validates arguments before any HIP call, and its workspace layout matches a re-derivation."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from video_dit_mixed_amd import binding as b
+from video_dit_mixed_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dap.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dap_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(b.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (dap_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_abi_version_and_status_strings():
+    assert b.abi_version() == 1
+    assert b.status_string(0) == "ok"
+    assert "workspace" in b.status_string(3)
+
+
+def _cfg(**kw):
+    return b.Config.from_workload(synth.workload(0), **kw)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), b.DAP_E_UNSUPPORTED),
+    (dict(region_h=3, region_w=3), b.DAP_E_UNSUPPORTED),
+    (dict(lam=1.5), b.DAP_E_INVALID),
+    (dict(lam=-0.1), b.DAP_E_INVALID),
+    (dict(lam=float("nan")), b.DAP_E_INVALID),
+    (dict(quota_bp=(5000, 3000, 2000, 1000)), b.DAP_E_INVALID),
+    (dict(quota_bp=(0, -1, 0, 100)), b.DAP_E_INVALID),
+    (dict(batch=0), b.DAP_E_INVALID),
+    (dict(T=0), b.DAP_E_INVALID),
+    (dict(T=200, H=48, W=96, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),   # > 4096 regions
+])
+def test_validation_rejects(kw, status):
+    with pytest.raises(b.DapError) as e:
+        b.workspace_bytes(_cfg(**kw))
+    assert e.value.status == status
+
+
+def test_calls_validate_before_touching_the_device():
+    """Null / misaligned pointers and short workspaces are refused on the host (no HIP call)."""
+    lib = b.load()
+    cfg = _cfg()
+    c = cfg.c_struct()
+    need = b.workspace_bytes(cfg)
+    P = ctypes.byref
+    assert lib.dap_prepare(P(c), None, None, None, None, need, None) == b.DAP_E_INVALID
+    assert lib.dap_prepare(None, 256, 256, 256, 256, need, None) == b.DAP_E_INVALID
+    assert lib.dap_prepare(P(c), 256, 256, 256, 256, need - 1, None) == b.DAP_E_WORKSPACE
+    assert lib.dap_prepare(P(c), 256, 256, 257, 256, need, None) == b.DAP_E_INVALID
+    assert lib.dap_draft_rank(P(c), 256, need - 1, None, None, None) == b.DAP_E_WORKSPACE
+    assert lib.dap_draft_rank(P(c), 256, need, 3, None, None) == b.DAP_E_INVALID
+    assert lib.dap_attention(P(c), 100, need, None) == b.DAP_E_INVALID
+    assert lib.dap_restore(P(c), 256, need, None, None) == b.DAP_E_INVALID
+    bad = _cfg(head_dim=32).c_struct()
+    assert lib.dap_attention(P(bad), 256, need, None) == b.DAP_E_UNSUPPORTED
+
+
+def _layout_py(w):
+    """Independent re-derivation of the documented workspace layout."""
+    al = lambda x: (x + 255) // 256 * 256
+    nby, nbx = -(-w.H // w.region_h), -(-w.W // w.region_w)
+    Nb = w.T * nby * nbx
+    B = w.region_h * w.region_w
+    Np, D, bh = Nb * B, w.head_dim, w.batch * w.heads
+    kp8 = -(-B // 64) * 64
+    sizes = [("q_bf16", bh * Np * D * 2), ("k_bf16", bh * Np * D * 2), ("vt_bf16", bh * Np * D * 2),
+             ("q_i8", bh * Np * D), ("k_i8", bh * Np * D), ("q_i8_scale", bh * Nb * 4),
+             ("k_i8_scale", bh * Nb * 4), ("q_fp4", bh * Np * D // 2), ("k_fp4", bh * Np * D // 2),
+             ("q_e8m0", bh * Np * D // 32), ("k_e8m0", bh * Np * D // 32),
+             ("vt_fp8", bh * Nb * D * kp8), ("v_scale", bh * D * 4), ("v_amax", bh * D * 4),
+             ("q_avg", bh * Nb * D * 8), ("q_max", bh * Nb * D * 8), ("k_avg", bh * Nb * D * 8),
+             ("k_max", bh * Nb * D * 8), ("scores", bh * Nb * Nb * 8), ("lmax", bh * Nb * Nb * 8),
+             ("rank_state", bh * 3 * 32), ("rank_hist", bh * 3 * 2048 * 4), ("map", bh * Nb * Nb),
+             ("lists", bh * Nb * Nb * 2), ("counts", bh * Nb * 16), ("out", bh * Np * D * 2)]
+    off, o = {}, 0
+    for name, n in sizes:
+        off["off_" + name] = o
+        o = al(o + n)
+    P = Nb * Nb
+    _, q4, q8, q16 = w.quota_bp
+    rnd = lambda x: (P * x + 5000) // 10000
+    return dict(off, total_bytes=o, Nb=Nb, B=B, Np=Np, kp8=kp8, Hp=nby * w.region_h,
+                Wp=nbx * w.region_w, pairs=P, c16=rnd(q16), c8=rnd(q16 + q8), c4=rnd(q16 + q8 + q4))
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workspace_layout_matches_rederivation(name):
+    w = synth.WORKLOADS[name]
+    L = b.workspace_layout(b.Config.from_workload(w))
+    exp = _layout_py(w)
+    for k, v in exp.items():
+        assert L[k] == v, k
+    assert b.workspace_bytes(b.Config.from_workload(w)) == exp["total_bytes"]
+    assert all(L[k] % 256 == 0 for k in L if k.startswith("off_"))
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        saved = b._lib
+        try:
+            b._lib = None
+            b.load(str(tmp_path / "nope.so"))
+        finally:
+            b._lib = saved

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars: pooled descriptors, quantised codes and scales, block maps, per-row lists and the restore
+permutation bit-exact; draft scores within 1e-12 relative; outputs within rel-L2 5e-3 and
+max-abs 2e-2 over real tokens.  Full-size workloads compare every head-level result of two sampled
+heads and the outputs of sampled query blocks (edge blocks with padding, the longest and shortest
+rows, and seeded random ones); the other heads carry copies of the sampled heads' inputs."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import draft as odraft, layout as olayout, pipeline as opipe
+from video_dit_mixed_amd import binding as b
+from video_dit_mixed_amd import synth
+
+from gpu_util import (Sections, bf16_bits, log, rel_l2, run_gpu, to_device, MAX_ABS_TOL,
+                      REL_L2_TOL, SCORE_RTOL)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(w, exact_heads=None):
+    """Exact generator output for `exact_heads` (all when None); the other heads copy them."""
+    if exact_heads is None:
+        return synth.make_inputs(w)
+    Q, K, V = synth.make_inputs(w, heads=exact_heads)
+    BH = w.batch * w.heads
+    src = list(exact_heads)
+    for i in range(BH):
+        if i in exact_heads:
+            continue
+        j = src[i % len(src)]
+        bb, h = divmod(i, w.heads)
+        sb, sh = divmod(j, w.heads)
+        Q[bb, h], K[bb, h], V[bb, h] = Q[sb, sh], K[sb, sh], V[sb, sh]
+    return Q, K, V
+
+
+def _oracle_head(w, Q, K, V, bhi):
+    bb, h = divmod(bhi, w.heads)
+    return opipe.prepare_head(Q[bb, h], K[bb, h], V[bb, h], T=w.T, H=w.H, W=w.W, rh=w.region_h,
+                              rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp)
+
+
+def _check_prep(S: Sections, r, L):
+    need16 = L["c16"] > 0
+    need8 = L["c8"] > L["c16"]
+    need4 = L["c4"] > L["c8"]
+    for name in ("q_avg", "q_max", "k_avg", "k_max"):
+        np.testing.assert_array_equal(getattr(S, name), getattr(r, name), err_msg=name)
+    if need16:
+        np.testing.assert_array_equal(S.q_bf16, bf16_bits(r.qp), err_msg="q bf16 pack")
+        np.testing.assert_array_equal(S.k_bf16, bf16_bits(r.kp), err_msg="k bf16 pack")
+        np.testing.assert_array_equal(S.vp_bf16, bf16_bits(r.vp), err_msg="v bf16 pack")
+    if need8:
+        np.testing.assert_array_equal(S.q_i8, r.q_i8, err_msg="q int8")
+        np.testing.assert_array_equal(S.k_i8, r.k_i8, err_msg="k int8")
+        np.testing.assert_array_equal(S.q_i8_s.view(np.uint32), r.q_i8_s.view(np.uint32))
+        np.testing.assert_array_equal(S.k_i8_s.view(np.uint32), r.k_i8_s.view(np.uint32))
+    if need4:
+        np.testing.assert_array_equal(S.q_fp4, r.q_fp4, err_msg="q mxfp4 codes")
+        np.testing.assert_array_equal(S.k_fp4, r.k_fp4, err_msg="k mxfp4 codes")
+        np.testing.assert_array_equal(S.q_e8, r.q_e8, err_msg="q e8m0")
+        np.testing.assert_array_equal(S.k_e8, r.k_e8, err_msg="k e8m0")
+    if need8 or need4:
+        np.testing.assert_array_equal(S.v_fp8, r.v_fp8, err_msg="v fp8 codes")
+        np.testing.assert_array_equal(S.v_s.view(np.uint32), r.v_s.view(np.uint32))
+
+
+def _check_map(S: Sections, r, L):
+    rel = np.abs(S.scores - r.A) / np.maximum(np.abs(r.A), 1e-300)
+    assert rel.max() <= SCORE_RTOL, f"draft scores rel err {rel.max():.3e}"
+    cuts = (int(L["c16"]), int(L["c8"]), int(L["c4"]))
+    assert cuts == r.cuts
+    # rank on the GPU's own scores: exact, no exceptions
+    own = odraft.assign_levels(odraft.rank_pairs(S.scores), cuts)
+    np.testing.assert_array_equal(S.map, own, err_msg="rank of the device's own scores")
+    # against the oracle's map: the only admissible difference is a pair within 1e-12 of a cut
+    diff = np.argwhere(S.map != r.levels)
+    if diff.size:
+        flat = r.A.ravel()
+        order = np.lexsort((np.arange(flat.size), -flat))
+        cut_scores = [flat[order[c - 1]] for c in cuts if 0 < c <= flat.size]
+        bad = [tuple(p) for p in diff
+               if not any(abs(r.A[tuple(p)] - cs) <= 1e-12 * cs for cs in cut_scores)]
+        log(f"map differs at {len(diff)} pairs, {len(bad)} not near a cut")
+        assert not bad
+    # per-row lists and counts
+    for qb in range(L["Nb"]):
+        row = S.map[qb]
+        n16, n8, n4 = (int((row == lv).sum()) for lv in (3, 2, 1))
+        assert tuple(S.counts[qb]) == (n16, n8, n4, 0)
+        lst = S.lists[qb]
+        np.testing.assert_array_equal(lst[:n16], np.flatnonzero(row == 3))
+        np.testing.assert_array_equal(lst[n16:n16 + n8], np.flatnonzero(row == 2))
+        np.testing.assert_array_equal(lst[n16 + n8:n16 + n8 + n4], np.flatnonzero(row == 1))
+
+
+def _check_out(S: Sections, r, blocks):
+    opipe.attend(r, q_blocks=blocks)
+    B = r.B
+    rows = np.concatenate([qb * B + np.flatnonzero(r.valid[qb]) for qb in blocks])
+    ref = r.out_packed[rows]
+    from oracle import quant
+    ref = quant.bf16_rne(ref)
+    got = synth.bf16_bits_to_f32(S.out_packed[rows]).astype(np.float64)
+    e_rel = rel_l2(got, ref)
+    e_max = np.abs(got - ref).max() if rows.size else 0.0
+    empty = sum(1 for qb in blocks if S.counts[qb][:3].sum() == 0)
+    log(f"out rows={rows.size} rel_l2={e_rel:.3e} max_abs={e_max:.3e} empty_rows={empty}")
+    assert e_rel <= REL_L2_TOL and e_max <= MAX_ABS_TOL
+    return e_rel, e_max
+
+
+def _check_restore(out, S_out_packed_all, L, w):
+    """The restored output equals the packed output under the oracle's token permutation."""
+    g = olayout.geometry(w.T, w.H, w.W, w.region_h, w.region_w)
+    src = olayout.source_index(g)
+    ok = src >= 0
+    got = out.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    for bhi, packed in S_out_packed_all:
+        bb, h = divmod(bhi, w.heads)
+        exp = np.empty((g.N, w.head_dim), np.uint16)
+        exp[src[ok]] = packed[ok]
+        np.testing.assert_array_equal(got[bb, h], exp)
+
+
+def _sample_blocks(r, S, k=12, seed=0):
+    Nb = r.g.Nb
+    kept = S.counts[:, :3].sum(1)
+    edge = [qb for qb in range(Nb) if not r.valid[qb].all()]
+    pick = {0, Nb - 1, int(np.argmax(kept)), int(np.argmin(kept))}
+    pick |= set(edge[:2]) | set(edge[-2:])
+    rng = np.random.default_rng(seed)
+    pick |= set(rng.choice(Nb, size=min(k, Nb), replace=False).tolist())
+    return sorted(pick)
+
+
+def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None):
+    log(f"case {w.name} quota={w.quota_bp} lam={w.lam} batch={w.batch}")
+    Q, K, V = _inputs(w, exact_heads)
+    cfg = b.Config.from_workload(w)
+    q, k, v = to_device(Q, K, V)
+    log("gpu run")
+    ws, out, L = run_gpu(cfg, q, k, v)
+    heads = check_heads if check_heads is not None else range(w.batch * w.heads)
+    packed = []
+    for bhi in heads:
+        log(f"head {bhi}: oracle")
+        r = _oracle_head(w, Q, K, V, bhi)
+        S = Sections(ws, L, bhi)
+        _check_prep(S, r, L)
+        _check_map(S, r, L)
+        blocks = list(range(r.g.Nb)) if sample_blocks is None else _sample_blocks(r, S, sample_blocks, bhi)
+        _check_out(S, r, blocks)
+        packed.append((bhi, S.out_packed))
+    _check_restore(out, packed, L, w)
+    return ws, out
+
+
+# ------------------------------------------------------------------------------------ workloads
+
+def test_parity_tiny_all_heads():
+    _run_case(synth.workload(0))
+
+
+def test_parity_mid_sampled_heads():
+    w = synth.workload(1)
+    _run_case(w, exact_heads=[0, 5, 11], check_heads=[0, 11])
+
+
+# ------------------------------------------------------------------------------------ phases alone
+
+@pytest.mark.parametrize("quota", [(0, 0, 0, 10000), (0, 0, 10000, 0), (0, 10000, 0, 0),
+                                   (5000, 5000, 0, 0), (4000, 2000, 2000, 2000)])
+@pytest.mark.parametrize("wi", [0, 1])
+def test_single_and_mixed_levels(wi, quota):
+    w = synth.workload(wi).with_(quota_bp=quota, heads=2)
+    _run_case(w)
+
+
+def test_dense_equals_plain_attention_on_gpu():
+    """Quotas 0/0/0/100: every pair is 16-bit, so the output is dense attention up to bf16 P."""
+    import torch
+    w = synth.workload(1).with_(quota_bp=(0, 0, 0, 10000), heads=2)
+    Q, K, V = synth.make_inputs(w)
+    cfg = b.Config.from_workload(w)
+    q, k, v = to_device(Q, K, V)
+    _, out, _ = run_gpu(cfg, q, k, v)
+    qf, kf, vf = (t.float().cpu() for t in (q, k, v))
+    ref = torch.softmax(qf @ kf.transpose(-1, -2) / np.sqrt(w.head_dim), dim=-1) @ vf
+    got = out.float().cpu()
+    rel = float((got - ref).norm() / ref.norm())
+    log(f"dense rel_l2={rel:.3e}")
+    assert rel <= REL_L2_TOL
+
+
+def test_all_skip_outputs_zero():
+    w = synth.workload(0).with_(quota_bp=(10000, 0, 0, 0))
+    Q, K, V = synth.make_inputs(w)
+    _, out, _ = run_gpu(b.Config.from_workload(w), *to_device(Q, K, V))
+    assert float(out.float().abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("lam", [0.0, 1.0])
+def test_lambda_endpoints(lam):
+    _run_case(synth.workload(0).with_(lam=lam))
+
+
+def test_batch_two():
+    _run_case(synth.workload(0).with_(batch=2))
+
+
+def test_ragged_odd_grid():
+    # regions that leave padding on both axes and an odd frame count
+    w = synth.Workload("ragged", 3, 13, 21, 2, 128, 8, 8, 0.5, (3000, 2500, 2500, 2000), seed=77)
+    _run_case(w)
+
+
+def test_deterministic_bitwise():
+    import torch
+    w = synth.workload(1).with_(heads=3)
+    Q, K, V = synth.make_inputs(w)
+    cfg = b.Config.from_workload(w)
+    q, k, v = to_device(Q, K, V)
+    ws1, out1, _ = run_gpu(cfg, q, k, v)
+    ws2, out2, _ = run_gpu(cfg, q, k, v)
+    L = b.workspace_layout(cfg)
+    assert torch.equal(out1, out2)
+    for name, dt, shape in (("map", torch.uint8, (L["bh"], L["Nb"], L["Nb"])),
+                            ("scores", torch.float64, (L["bh"], L["Nb"], L["Nb"]))):
+        assert torch.equal(b.section(ws1, L, name, dt, shape), b.section(ws2, L, name, dt, shape))
+
+
+# ------------------------------------------------------------------------------------ full size
+
+@pytest.mark.parametrize("wi", [2, 3, 4])
+def test_parity_full_size(wi):
+    w = synth.workload(wi)
+    _run_case(w, exact_heads=[0, w.heads - 1], sample_blocks=10, check_heads=[0, w.heads - 1])

@@ -1,0 +1,392 @@
+// Mixed-precision block-sparse attention with precision phases (gfx950 matrix cores).
+//
+// Method: "DraftAttention2" -- newx.sg paper card, Abstract (one attention kernel with
+// precision-specific phases sharing data movement, softmax statistics and output accumulation);
+// pchao.org blog, section 方法概览 bullet 4 (phases share the softmax statistics and the output
+// accumulation and rescale by the quantisation scales at phase boundaries; no per-precision
+// write-back and merge) and bullet 2 (16-bit, INT8 and 4-bit blocks).
+//
+// One workgroup per (head, query block); wave w owns queries 32w..32w+31 of the block.  For every
+// kept key block, in phase order 16 -> 8 -> 4 and ascending kb inside a phase:
+//   S^T = K Q^T on the matrix cores (keys are the MFMA rows, so each lane holds one query column
+//         and a query's scores live in two lanes: row statistics need one cross-lane step)
+//         16-bit: v_mfma_f32_32x32x16_bf16        8-bit: v_mfma_i32_32x32x32_i8 (x s_q s_k)
+//         4-bit:  v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands and E8M0 block scales
+//   online softmax in registers in the log2 domain (one running-max update per key block):
+//         m' = max(m, rowmax t), alpha = 2^(m - m'), P = 2^(t - m'), l = alpha l + sum P
+//   O^T += V^T P^T on the matrix cores, P converted in registers to the B operand layout:
+//         16-bit: bf16(P) x bf16 V        low-bit: e4m3(2^8 P) x e4m3 V (scaled f8f6f4 MFMA)
+// One fp32 accumulator serves all phases.  At the first low-bit block its channel d is converted
+// to low-bit units (x 2^8 / s_V[d]); the end multiplies by s_V[d] 2^-8 and divides by l.
+// Key and V tiles are staged through LDS with 16-byte-staggered rows (bank-conflict-free reads);
+// the matrix-core operand orders were fixed when the operands were packed, so every LDS read is
+// one or two 16-byte loads per lane.
+#include "dap_internal.h"
+
+namespace dap {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(16))) int i32x16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kScaleOne = 0x7f7f7f7f;  // E8M0 127 = 2^0 in every byte
+
+template <int B, int D>
+struct AttnCfg {
+  static constexpr int NW = B >= 32 ? B / 32 : 1;  // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int KT = B >= 32 ? B : 32;      // key slots covered by the S^T m-tiles
+  static constexpr int MT = KT / 32;               // S^T m-tiles (32 keys each)
+  static constexpr int DT = D / 32;                // O^T m-tiles (32 channels each)
+  static constexpr int KP8 = (B + 63) / 64 * 64;   // FP8 V^T row length
+  static constexpr int KSTR16 = 2 * D + 16;        // LDS row strides (bytes)
+  static constexpr int KSTR8 = D + 16;
+  static constexpr int KSTR4 = D / 2 + 16;
+  static constexpr int VSTR16 = 2 * B + 16;
+  static constexpr int VSTR8 = KP8 + 16;
+  static constexpr int KBYTES = KT * KSTR16;
+  static constexpr int VBYTES = (D * VSTR16 > D * VSTR8) ? D * VSTR16 : D * VSTR8;
+  static constexpr int SBYTES = KT * (D / 32);
+};
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Per-workgroup context of one (head, query block) row.
+struct RowCtx {
+  int bh, qb, tid, n, gh;
+  bool qok;
+  size_t qrow;            // packed row of this lane's query
+  const uint16_t* list;   // key-block list of the row
+};
+
+// Copy ROWS rows of CPR 16-byte chunks from global (row stride GS bytes) to LDS (row stride LS
+// bytes) with NT threads; rows >= valid are written as zeros.  Every thread keeps one global and
+// one LDS base address; the per-pass offsets are compile-time constants.
+template <int ROWS, int CPR, int NT, int GS, int LS>
+__device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ gsrc, uint8_t* ldst, int tid,
+                                          int valid) {
+  constexpr int RPP = NT / CPR;
+  constexpr int PASSES = (ROWS + RPP - 1) / RPP;
+  const int r0 = tid / CPR, cc = tid - (tid / CPR) * CPR;
+  const uint8_t* gp = gsrc + (size_t)r0 * GS + cc * 16;
+  uint8_t* lp = ldst + r0 * LS + cc * 16;
+  uint4 v[PASSES];
+#pragma unroll
+  for (int j = 0; j < PASSES; ++j) {
+    const int r = r0 + j * RPP;
+    v[j] = (r < ROWS && r < valid) ? *reinterpret_cast<const uint4*>(gp + (size_t)j * RPP * GS)
+                                   : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < PASSES; ++j)
+    if (r0 + j * RPP < ROWS) *reinterpret_cast<uint4*>(lp + j * RPP * LS) = v[j];
+}
+
+template <int B, int D>
+__device__ __forceinline__ void stage_tile(const Geo& g, const Ws& w, const RowCtx& c, int phase,
+                                           int kb, uint8_t* sK, uint8_t* sV, uint8_t* sKs) {
+  using C = AttnCfg<B, D>;
+  const size_t krow0 = (size_t)c.bh * g.Np + (size_t)kb * B;
+  const int tid = c.tid;
+  if (phase == 0) {
+    copy_rows<C::KT, 2 * D / 16, C::NT, 2 * D, C::KSTR16>(
+        reinterpret_cast<const uint8_t*>(w.k_bf16 + krow0 * D), sK, tid, B);
+    copy_rows<D, 2 * B / 16, C::NT, 2 * B, C::VSTR16>(
+        reinterpret_cast<const uint8_t*>(w.vt_bf16 + ((size_t)c.bh * g.Nb + kb) * (size_t)D * B), sV,
+        tid, D);
+    return;
+  }
+  if (phase == 1) {
+    copy_rows<C::KT, D / 16, C::NT, D, C::KSTR8>(
+        reinterpret_cast<const uint8_t*>(w.k_i8 + krow0 * D), sK, tid, B);
+  } else {
+    copy_rows<C::KT, D / 32, C::NT, D / 2, C::KSTR4>(w.k_fp4 + krow0 * (D / 2), sK, tid, B);
+    const uint8_t* esrc = w.k_e8m0 + krow0 * (D / 32);
+    for (int i = tid; i < C::KT * (D / 32); i += C::NT)
+      sKs[i] = i < B * (D / 32) ? esrc[i] : (uint8_t)127;
+  }
+  copy_rows<D, C::KP8 / 16, C::NT, C::KP8, C::VSTR8>(
+      w.vt_fp8 + ((size_t)c.bh * g.Nb + kb) * (size_t)D * C::KP8, sV, tid, D);
+}
+
+// All key blocks of one precision phase (PH = 0: 16-bit, 1: 8-bit, 2: 4-bit) for this row.
+// Only this phase's Q operand is live, so the three phases do not compete for registers.
+template <int B, int D, int PH>
+__device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCtx& c,
+                                          f32x16 (&O)[AttnCfg<B, D>::DT], float& m_run,
+                                          float& l_run, int np, int off, uint8_t* sK, uint8_t* sV,
+                                          uint8_t* sKs, float* sBias) {
+  using C = AttnCfg<B, D>;
+  const int n = c.n, gh = c.gh;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+
+  // Q operand for this phase, straight from the packed workspace
+  constexpr int NQ = PH == 0 ? D / 16 : (PH == 1 ? D / 32 : D / 64);
+  uint4 qop[NQ];
+  int qsc[NQ];
+  float s_q = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < NQ; ++ks) {
+    const uint8_t* base =
+        PH == 0 ? reinterpret_cast<const uint8_t*>(w.q_bf16 + c.qrow * D) + 32 * ks + 16 * gh
+        : PH == 1 ? reinterpret_cast<const uint8_t*>(w.q_i8 + c.qrow * D) + 32 * ks + 16 * gh
+                  : w.q_fp4 + c.qrow * (D / 2) + 32 * ks + 16 * gh;
+    qop[ks] = c.qok ? *reinterpret_cast<const uint4*>(base) : make_uint4(0, 0, 0, 0);
+    qsc[ks] = (PH == 2 && c.qok) ? (int)w.q_e8m0[c.qrow * (D / 32) + 2 * ks + gh] : 127;
+  }
+  if (PH == 1) s_q = w.q_i8_scale[(size_t)c.bh * g.Nb + c.qb];
+
+  for (int it = 0; it < np; ++it) {
+    const int kb = c.list[off + it];
+    // real extent of key block kb (regions at the high-y / high-x edge hold padding)
+    const int per = g.nby * g.nbx;
+    const int rem = kb % per;
+    const int ry = rem / g.nbx, rx = rem - ry * g.nbx;
+    const int vh = min(g.rh, g.H - ry * g.rh), vw = min(g.rw, g.W - rx * g.rw);
+    const bool full = vh == g.rh && vw == g.rw && B == C::KT;
+    __syncthreads();  // previous tile fully consumed
+    stage_tile<B, D>(g, w, c, PH, kb, sK, sV, sKs);
+    if (!full && c.tid < C::KT) {
+      const int m = c.tid, iy = m / g.rw, ix = m - (m / g.rw) * g.rw;
+      sBias[m] = (m < B && iy < vh && ix < vw) ? 0.0f : -INFINITY;
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T
+    f32x16 S[C::MT];
+    float c_scale = kLog2e * inv_sqrt_d;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      const int krow = 32 * mt + n;
+      if (PH == 0) {
+        f32x16 acc = {};
+        const uint8_t* rowp = sK + krow * C::KSTR16 + 16 * gh;
+#pragma unroll
+        for (int ks = 0; ks < NQ; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lds16(rowp + 32 * ks)),
+                                                        __builtin_bit_cast(bf16x8, qop[ks]), acc, 0, 0, 0);
+        S[mt] = acc;
+      } else if (PH == 1) {
+        i32x16 acc = {};
+        const uint8_t* rowp = sK + krow * C::KSTR8 + 16 * gh;
+#pragma unroll
+        for (int ks = 0; ks < NQ; ++ks)
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, lds16(rowp + 32 * ks)),
+                                                      __builtin_bit_cast(i32x4, qop[ks]), acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[mt][r] = (float)acc[r];
+      } else {
+        f32x16 acc = {};
+        const uint8_t* rowp = sK + krow * C::KSTR4 + 16 * gh;
+#pragma unroll
+        for (int ks = 0; ks < NQ; ++ks) {
+          const uint4 u = lds16(rowp + 32 * ks);
+          const i32x8 a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+          const i32x8 b = {(int)qop[ks].x, (int)qop[ks].y, (int)qop[ks].z, (int)qop[ks].w, 0, 0, 0, 0};
+          const int ksc = (int)sKs[krow * (D / 32) + 2 * ks + gh];
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, 0, ksc, 0, qsc[ks]);
+        }
+        S[mt] = acc;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // bound operand lookahead to one m-tile
+    }
+    if (PH == 1) c_scale = s_q * w.k_i8_scale[(size_t)c.bh * g.Nb + kb] * (kLog2e * inv_sqrt_d);
+
+    // ---- scale to the log2 domain; pad keys (and key slots beyond B) get -inf from sBias
+    if (full) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[mt][r] *= c_scale;
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 bias4 = *reinterpret_cast<const float4*>(sBias + 32 * mt + 8 * r4 + 4 * gh);
+          S[mt][4 * r4 + 0] = S[mt][4 * r4 + 0] * c_scale + bias4.x;
+          S[mt][4 * r4 + 1] = S[mt][4 * r4 + 1] * c_scale + bias4.y;
+          S[mt][4 * r4 + 2] = S[mt][4 * r4 + 2] * c_scale + bias4.z;
+          S[mt][4 * r4 + 3] = S[mt][4 * r4 + 3] * c_scale + bias4.w;
+        }
+    }
+
+    // ---- online softmax (log2 domain), one running-max update per key block
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float bias = PH == 0 ? m_new : m_new - 8.0f;  // low-bit phases produce 2^8 P
+    float psum = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(S[mt][r] - bias);
+        S[mt][r] = p;
+        psum += p;
+      }
+    if (PH != 0) psum *= 0.00390625f;  // 2^-8, exact
+    l_run = alpha * l_run + psum;
+    m_run = m_new;
+    if (!__all(alpha == 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T
+    if (PH == 0) {
+#pragma unroll
+      for (int c16 = 0; c16 < B / 16; ++c16) {
+        const int mt = c16 >> 1, rb = 8 * (c16 & 1);
+        bf16x8 bop;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bop[j] = (__bf16)S[mt][rb + j];
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, lds16(sV + (32 * dt + n) * C::VSTR16 + (16 * c16 + 8 * gh) * 2));
+          O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, O[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int c64 = 0; c64 < C::KP8 / 64; ++c64) {
+        i32x8 bop;
+#pragma unroll
+        for (int hsel = 0; hsel < 2; ++hsel) {
+          const int mt = 2 * c64 + hsel;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            int word = 0;
+            if (mt < C::MT) {
+              word = __builtin_amdgcn_cvt_pk_fp8_f32(S[mt][4 * q4 + 0], S[mt][4 * q4 + 1], word, false);
+              word = __builtin_amdgcn_cvt_pk_fp8_f32(S[mt][4 * q4 + 2], S[mt][4 * q4 + 3], word, true);
+            }
+            bop[4 * hsel + q4] = word;
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const uint8_t* vp = sV + (32 * dt + n) * C::VSTR8 + 64 * c64 + 32 * gh;
+          const uint4 u0 = lds16(vp), u1 = lds16(vp + 16);
+          const i32x8 a = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                           (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+          O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, O[dt], 0, 0, 0, kScaleOne,
+                                                                  0, kScaleOne);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+template <int B, int D>
+__global__ __launch_bounds__(64 * (B >= 32 ? B / 32 : 1)) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_kernel(Geo g, Ws w) {
+  using C = AttnCfg<B, D>;
+  __shared__ __attribute__((aligned(16))) uint8_t sK[C::KBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[C::VBYTES];
+  __shared__ uint8_t sKs[C::SBYTES];
+  __shared__ __attribute__((aligned(16))) float sBias[C::KT];
+
+  RowCtx c;
+  const int Nb = g.Nb;
+  c.bh = blockIdx.x / Nb;
+  c.qb = blockIdx.x - c.bh * Nb;
+  c.tid = threadIdx.x;
+  const int wv = c.tid >> 6, lane = c.tid & 63;
+  c.n = lane & 31;
+  c.gh = lane >> 5;
+  const int qr = 32 * wv + c.n;  // query row inside the block
+  c.qok = qr < B;
+  c.qrow = (size_t)c.bh * g.Np + (size_t)c.qb * B + qr;
+  c.list = w.lists + (size_t)c.bh * g.pairs + (size_t)c.qb * Nb;
+
+  const int32_t* cnt = w.counts + ((size_t)c.bh * Nb + c.qb) * 4;
+  const int n16 = __builtin_amdgcn_readfirstlane(cnt[0]);
+  const int n8 = __builtin_amdgcn_readfirstlane(cnt[1]);
+  const int n4 = __builtin_amdgcn_readfirstlane(cnt[2]);
+
+  f32x16 O[C::DT];
+#pragma unroll
+  for (int i = 0; i < C::DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[i][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  if (n16 > 0) run_phase<B, D, 0>(g, w, c, O, m_run, l_run, n16, 0, sK, sV, sKs, sBias);
+  const bool lowbit = n8 + n4 > 0;
+  if (lowbit) {
+    // accumulator unit change at the 16 -> low-bit boundary: channel d x 2^8 / s_V[d]
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * dt + 8 * (r >> 2) + 4 * c.gh + (r & 3);
+        const float sv = w.v_scale[(size_t)c.bh * D + d];
+        O[dt][r] *= sv > 0.0f ? 256.0f / sv : 0.0f;
+      }
+  }
+  if (n8 > 0) run_phase<B, D, 1>(g, w, c, O, m_run, l_run, n8, n16, sK, sV, sKs, sBias);
+  if (n4 > 0) run_phase<B, D, 2>(g, w, c, O, m_run, l_run, n4, n16 + n8, sK, sV, sKs, sBias);
+
+  // ---- finalise: O / l (0 when no pair was kept), undo the low-bit units, bf16 out
+  const float l = l_run + __shfl_xor(l_run, 32);
+  const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+  if (c.qok) {
+    uint16_t* dst = w.out + c.qrow * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * dt + 8 * r4 + 4 * c.gh;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float o = O[dt][4 * r4 + e];
+          if (lowbit) o *= w.v_scale[(size_t)c.bh * D + d0 + e] * 0.00390625f;
+          v[e] = o * inv_l;
+        }
+        const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1], b2 = (__bf16)v[2], b3 = (__bf16)v[3];
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+        *reinterpret_cast<uint2*>(dst + d0) = make_uint2(lo, hi);
+      }
+  }
+}
+
+template <int B, int D>
+hipError_t attn_bd(const Geo& g, const Ws& w, hipStream_t s) {
+  using C = AttnCfg<B, D>;
+  attn_kernel<B, D><<<(unsigned)(g.bh * g.Nb), C::NT, 0, s>>>(g, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const Geo& g, const Ws& w, hipStream_t s) {
+  if (g.D == 64) {
+    if (g.B == 16) return attn_bd<16, 64>(g, w, s);
+    if (g.B == 64) return attn_bd<64, 64>(g, w, s);
+    return attn_bd<128, 64>(g, w, s);
+  }
+  if (g.B == 16) return attn_bd<16, 128>(g, w, s);
+  if (g.B == 64) return attn_bd<64, 128>(g, w, s);
+  return attn_bd<128, 128>(g, w, s);
+}
+
+}  // namespace dap

@@ -1,0 +1,80 @@
+// Internal definitions shared by the libdap translation units (host launchers + gfx950 kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dap.h"
+
+namespace dap {
+
+// Everything a kernel needs to know about one layer, passed by value.
+struct Geo {
+  int bh, heads, D;
+  int T, H, W, rh, rw;
+  int Hp, Wp, nby, nbx, Nb, B, Np, kp8;
+  int N;
+  long long pairs, c16, c8, c4;
+  double lambda;
+  int need16, need8, need4;  // does any pair use this precision
+};
+
+// Device pointers to the workspace sections.
+struct Ws {
+  uint16_t* q_bf16;
+  uint16_t* k_bf16;
+  uint16_t* vt_bf16;
+  int8_t* q_i8;
+  int8_t* k_i8;
+  float* q_i8_scale;
+  float* k_i8_scale;
+  uint8_t* q_fp4;
+  uint8_t* k_fp4;
+  uint8_t* q_e8m0;
+  uint8_t* k_e8m0;
+  uint8_t* vt_fp8;
+  float* v_scale;
+  uint32_t* v_amax;
+  double* q_avg;
+  double* q_max;
+  double* k_avg;
+  double* k_max;
+  double* scores;
+  double* lmax;
+  void* rank_state;
+  uint32_t* rank_hist;
+  uint8_t* map;
+  uint16_t* lists;
+  int32_t* counts;
+  uint16_t* out;
+};
+
+// Ranking: an 87-bit key per pair, ascending key = (score descending, pair index ascending):
+//   key = ((~bits(score) & 0x7fff'ffff'ffff'ffff) << 24) | pair_index, pair_index < 2^24.
+// The cut of each level is found by an MSD radix select with 8 digits (7 x 11 bits + 10 bits).
+constexpr int kRankDigits = 8;
+constexpr int kRankBins = 2048;
+enum RankMode : int { kCutNone = 0, kCutAll = 1, kCutKey = 2 };
+struct RankCut {
+  unsigned long long prefix_hi;  // key bits known so far (a 128-bit integer, hi/lo halves)
+  unsigned long long prefix_lo;
+  long long remaining;           // rank still to skip inside the current prefix bucket
+  int mode;
+  int pad;
+};
+
+__host__ __device__ constexpr int rank_digit_width(int k) { return k == kRankDigits - 1 ? 10 : 11; }
+// bits below digit k: 76, 65, 54, 43, 32, 21, 10, 0
+__host__ __device__ constexpr int rank_digit_shift(int k) {
+  return k == kRankDigits - 1 ? 0 : 87 - 11 * (k + 1);
+}
+
+// Launchers (each returns hipGetLastError() of its launches).
+hipError_t launch_prepare(const Geo& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const Ws& w, hipStream_t s);
+hipError_t launch_draft(const Geo& g, const Ws& w, hipStream_t s);
+hipError_t launch_rank(const Geo& g, const Ws& w, hipStream_t s);
+hipError_t launch_attention(const Geo& g, const Ws& w, hipStream_t s);
+hipError_t launch_restore(const Geo& g, const Ws& w, uint16_t* out, hipStream_t s);
+
+}  // namespace dap

@@ -1,0 +1,418 @@
+// Operand preparation (gfx950): region reorder + padding, avg/max pooling, INT8 and MXFP4
+// quantisation of Q and K in one pass over each tensor; V absmax, then V reorder + transpose +
+// pack into the bf16 and FP8 matrix-core layouts.
+//
+// Method: "DraftAttention2" -- pchao.org blog, section 方法概览 bullet 4 (reorder, pooling and
+// quantisation of Q/K share one preparation kernel) and the Figure 3 caption (compact spatial
+// regions packed into contiguous blocks with gray padding; V reordering and transposition fused
+// with operand packing).  Pooling: section 方法概览 bullet 1 (average and channel-wise max
+// descriptor per region).
+//
+// Number formats (exact, so codes match a reference bit for bit):
+//   INT8 per (head, block):   a = max|x| over the block, r = 127/a (fp32, correctly rounded),
+//                             code = clamp(rne(x*r), -127, 127), scale = a/127; a = 0 -> all 0.
+//   MXFP4 per (row, 32 ch):   e = clamp(floor(log2 amax) - 2, -127, 127) (amax = 0 -> -127),
+//                             byte = e + 127, code = E2M1 rne saturating of x*2^-e, sign = sign
+//                             bit of x; two codes per byte, even channel in the low nibble.
+//   FP8 V per (head, ch):     a_d = max|V[:, d]| over real tokens, r = 448/a_d,
+//                             code = e4m3fn rne saturating of x*r, scale = a_d/448.
+// Launch shapes: prep_qk one 256-thread workgroup per (block, head, tensor); v_amax a grid of
+// token slices per head; v_pack one workgroup per (block, head).  Reads are whole region rows
+// (region_w * D * 2 contiguous bytes) with 16-byte lanes.
+#pragma clang fp contract(off)
+
+#include "dap_internal.h"
+
+namespace dap {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Unpack a 16-byte chunk of 8 bf16 values.
+__device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
+  x[0] = bf16_to_f32(u.x & 0xffff);
+  x[1] = bf16_to_f32(u.x >> 16);
+  x[2] = bf16_to_f32(u.y & 0xffff);
+  x[3] = bf16_to_f32(u.y >> 16);
+  x[4] = bf16_to_f32(u.z & 0xffff);
+  x[5] = bf16_to_f32(u.z >> 16);
+  x[6] = bf16_to_f32(u.w & 0xffff);
+  x[7] = bf16_to_f32(u.w >> 16);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// E2M1 magnitude code of |v| (round to nearest, ties to the even code, saturate at 6).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
+         (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
+         (uint32_t)(v > 5.0f);
+}
+
+// MX shared exponent of a group whose max magnitude is amax (a bf16 value held in fp32).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const uint32_t ef = (__float_as_uint(amax) >> 23) & 0xff;
+  if (amax == 0.0f || ef == 0) return -127;  // zero or subnormal: floor(log2) - 2 < -127
+  int e = (int)ef - 127 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// fp32 -> e4m3fn byte, round to nearest even, saturating at 448; sign from the sign bit.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float mag = fabsf(y);
+  uint32_t code;
+  if (mag >= 448.0f) {
+    code = 0x7e;
+  } else {
+    int E = (int)((bits >> 23) & 0xff) - 127;
+    if (E < -6) {
+      code = (uint32_t)rintf(mag * 512.0f);  // subnormal quantum 2^-9; 8 means 2^-6 (code 0x08)
+    } else {
+      uint32_t m = (uint32_t)rintf(ldexpf(mag, 3 - E));  // in [8, 16]
+      if (m == 16) {
+        E += 1;
+        m = 8;
+      }
+      code = ((uint32_t)(E + 7) << 3) | (m - 8);
+    }
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+struct BlockCoord {
+  int t, ry, rx, vh, vw;
+};
+
+__device__ __forceinline__ BlockCoord block_coord(const Geo& g, int b) {
+  BlockCoord c;
+  const int per = g.nby * g.nbx;
+  c.t = b / per;
+  const int rem = b - c.t * per;
+  c.ry = rem / g.nbx;
+  c.rx = rem - c.ry * g.nbx;
+  c.vh = min(g.rh, g.H - c.ry * g.rh);
+  c.vw = min(g.rw, g.W - c.rx * g.rw);
+  return c;
+}
+
+// ------------------------------------------------------------------------------------ Q / K
+template <int D>
+__global__ __launch_bounds__(kThreads) void prep_qk_kernel(Geo g, const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k, Ws w) {
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int RP = kThreads / CH;   // rows per pass
+  constexpr int MAXP = 128 / RP;      // passes for the largest block (128 rows)
+  __shared__ double s_sum[RP][D];
+  __shared__ float s_max[RP][D];
+  __shared__ float s_red[kThreads / 64];
+
+  const int b = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
+  const uint16_t* src = (tensor == 0 ? q : k) + (size_t)bh * g.N * D;
+  const int tid = threadIdx.x;
+  const int c = tid % CH;
+  const int r0 = tid / CH;
+  const int B = g.B;
+  const BlockCoord bc = block_coord(g, b);
+
+  uint4 raw[MAXP];
+  bool ok[MAXP];
+  bool inblk[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const int r = r0 + p * RP;
+    raw[p] = make_uint4(0, 0, 0, 0);
+    ok[p] = false;
+    inblk[p] = r < B;
+    if (r < B) {
+      const int iy = r / g.rw, ix = r - (r / g.rw) * g.rw;
+      if (iy < bc.vh && ix < bc.vw) {
+        const size_t n = ((size_t)bc.t * g.H + bc.ry * g.rh + iy) * g.W + bc.rx * g.rw + ix;
+        raw[p] = *reinterpret_cast<const uint4*>(src + n * D + c * 8);
+        ok[p] = true;
+      }
+    }
+  }
+
+  const size_t row0 = (size_t)bh * g.Np + (size_t)b * B;  // first packed row of this block
+
+  // bf16 packed copy
+  if (g.need16) {
+    uint16_t* dst = tensor == 0 ? w.q_bf16 : w.k_bf16;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p)
+      if (inblk[p])
+        *reinterpret_cast<uint4*>(dst + (row0 + r0 + p * RP) * D + c * 8) = raw[p];
+  }
+
+  // per-thread partial pooling and block absmax
+  double psum[8];
+  float pmax[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    psum[j] = 0.0;
+    pmax[j] = -INFINITY;
+  }
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    float x[8];
+    unpack8(raw[p], x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      amax = fmaxf(amax, fabsf(x[j]));
+      if (ok[p]) {
+        psum[j] += (double)x[j];
+        pmax[j] = fmaxf(pmax[j], x[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s_sum[r0][c * 8 + j] = psum[j];
+    s_max[r0][c * 8 + j] = pmax[j];
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) s_red[tid >> 6] = amax;
+  __syncthreads();
+  amax = s_red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) amax = fmaxf(amax, s_red[i]);
+
+  // pooled descriptors: channel d = tid (fixed summation order over the RP partials)
+  if (tid < D) {
+    double s = 0.0;
+    float m = -INFINITY;
+    for (int i = 0; i < RP; ++i) {
+      s += s_sum[i][tid];
+      m = fmaxf(m, s_max[i][tid]);
+    }
+    const size_t o = ((size_t)bh * g.Nb + b) * D + tid;
+    const double nvalid = (double)(bc.vh * bc.vw);
+    if (tensor == 0) {
+      w.q_avg[o] = s / nvalid;
+      w.q_max[o] = (double)m;
+    } else {
+      w.k_avg[o] = s / nvalid;
+      w.k_max[o] = (double)m;
+    }
+  }
+
+  // INT8 per block
+  if (g.need8) {
+    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+    int8_t* dst = tensor == 0 ? w.q_i8 : w.k_i8;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+      if (!inblk[p]) continue;
+      float x[8];
+      unpack8(raw[p], x);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float cv = rintf(x[j] * r);
+        cv = fminf(fmaxf(cv, -127.0f), 127.0f);
+        const uint32_t byte = (uint32_t)((int)cv) & 0xffu;
+        if (j < 4) lo |= byte << (8 * j);
+        else hi |= byte << (8 * (j - 4));
+      }
+      *reinterpret_cast<uint2*>(dst + (row0 + r0 + p * RP) * D + c * 8) = make_uint2(lo, hi);
+    }
+    if (tid == 0) {
+      float* sc = tensor == 0 ? w.q_i8_scale : w.k_i8_scale;
+      sc[(size_t)bh * g.Nb + b] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    }
+  }
+
+  // MXFP4 per (row, 32-channel group): a group is 4 adjacent lanes (chunks 4G..4G+3)
+  if (g.need4) {
+    uint8_t* dst = tensor == 0 ? w.q_fp4 : w.k_fp4;
+    uint8_t* dse = tensor == 0 ? w.q_e8m0 : w.k_e8m0;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+      float x[8];
+      unpack8(raw[p], x);
+      float ga = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ga = fmaxf(ga, fabsf(x[j]));
+      ga = fmaxf(ga, __shfl_xor(ga, 1));
+      ga = fmaxf(ga, __shfl_xor(ga, 2));
+      if (!inblk[p]) continue;
+      const int e = mx_exponent(ga);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sgn = (word_of(raw[p], j >> 1) >> ((j & 1) ? 31 : 15)) & 1u;
+        const uint32_t code = e2m1_code(fabsf(ldexpf(x[j], -e))) | (sgn << 3);
+        packed |= code << (4 * j);
+      }
+      const size_t row = row0 + r0 + p * RP;
+      *reinterpret_cast<uint32_t*>(dst + row * (D / 2) + c * 4) = packed;
+      if ((c & 3) == 0) dse[row * (D / 32) + (c >> 2)] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------ V absmax
+template <int D>
+__global__ __launch_bounds__(kThreads) void v_amax_kernel(Geo g, const uint16_t* __restrict__ v,
+                                                         uint32_t* __restrict__ amax_bits,
+                                                         int tokens_per_slice) {
+  constexpr int CH = D / 8;
+  constexpr int RP = kThreads / CH;
+  __shared__ float s_max[RP][D];
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, c = tid % CH, r0 = tid / CH;
+  const int n0 = blockIdx.x * tokens_per_slice;
+  const int n1 = min(g.N, n0 + tokens_per_slice);
+  const uint16_t* src = v + (size_t)bh * g.N * D;
+  float m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = 0.0f;
+  for (int n = n0 + r0; n < n1; n += RP) {
+    float x[8];
+    unpack8(*reinterpret_cast<const uint4*>(src + (size_t)n * D + c * 8), x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(x[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s_max[r0][c * 8 + j] = m[j];
+  __syncthreads();
+  if (tid < D) {
+    float a = 0.0f;
+    for (int i = 0; i < RP; ++i) a = fmaxf(a, s_max[i][tid]);
+    atomicMax(&amax_bits[(size_t)bh * D + tid], __float_as_uint(a));  // a >= 0: bits are ordered
+  }
+}
+
+// Position of key m of a block inside the bf16 V^T row: within each 16-key chunk the stored
+// order is keys 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of m swapped).
+__device__ __forceinline__ int vt16_pos(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// Position of key m inside the FP8 V^T row: within each 64-key chunk, key
+// 32a + 8b + 4g + e (a in 0..1, b in 0..3, g in 0..1, e in 0..3) sits at 32g + 16a + 4b + e.
+__device__ __forceinline__ int vt8_pos(int m) {
+  const int k = m & 63;
+  return (m & ~63) | (((k >> 2) & 1) << 5) | (((k >> 5) & 1) << 4) | (((k >> 3) & 3) << 2) |
+         (k & 3);
+}
+
+// ------------------------------------------------------------------------------------ V pack
+template <int D>
+__global__ __launch_bounds__(kThreads) void v_pack_kernel(Geo g, const uint16_t* __restrict__ v,
+                                                         Ws w) {
+  constexpr int CH = D / 8;
+  constexpr int RP = kThreads / CH;
+  constexpr int MAXP = 128 / RP;
+  constexpr int KPMAX = 128;                      // largest B and kp8
+  __shared__ uint16_t s_vt16[D][KPMAX + 8];       // +8 elements: stagger LDS rows
+  __shared__ uint8_t s_vt8[D][KPMAX + 16];
+  __shared__ float s_r[D];
+
+  const int b = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, c = tid % CH, r0 = tid / CH;
+  const int B = g.B, kp8 = g.kp8;
+  const BlockCoord bc = block_coord(g, b);
+  const uint16_t* src = v + (size_t)bh * g.N * D;
+
+  if (tid < D) {
+    const float a = __uint_as_float(w.v_amax[(size_t)bh * D + tid]);
+    s_r[tid] = a > 0.0f ? 448.0f / a : 0.0f;
+    if (b == 0) w.v_scale[(size_t)bh * D + tid] = a > 0.0f ? a / 448.0f : 0.0f;
+  }
+  // zero the unused FP8 positions (keys >= B when B < 64)
+  for (int i = tid; i < D * kp8; i += kThreads) {
+    const int d = i / kp8, pos = i - (i / kp8) * kp8;
+    s_vt8[d][pos] = 0;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const int r = r0 + p * RP;
+    if (r >= B) continue;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    const int iy = r / g.rw, ix = r - (r / g.rw) * g.rw;
+    if (iy < bc.vh && ix < bc.vw) {
+      const size_t n = ((size_t)bc.t * g.H + bc.ry * g.rh + iy) * g.W + bc.rx * g.rw + ix;
+      raw = *reinterpret_cast<const uint4*>(src + n * D + c * 8);
+    }
+    const int p16 = vt16_pos(r), p8 = vt8_pos(r);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = (word_of(raw, j >> 1) >> ((j & 1) ? 16 : 0)) & 0xffffu;
+      const int d = c * 8 + j;
+      s_vt16[d][p16] = (uint16_t)h;
+      s_vt8[d][p8] = (uint8_t)e4m3_code(bf16_to_f32(h) * s_r[d]);
+    }
+  }
+  __syncthreads();
+
+  // write rows d: bf16 row of B elements, fp8 row of kp8 bytes (8-byte lanes)
+  if (g.need16) {
+    uint16_t* dst = w.vt_bf16 + ((size_t)bh * g.Nb + b) * (size_t)D * B;
+    const int per_row = B / 4;  // 8-byte chunks
+    for (int i = tid; i < D * per_row; i += kThreads) {
+      const int d = i / per_row, ch = i - (i / per_row) * per_row;
+      const uint16_t* s = &s_vt16[d][ch * 4];
+      uint2 val = make_uint2((uint32_t)s[0] | ((uint32_t)s[1] << 16),
+                             (uint32_t)s[2] | ((uint32_t)s[3] << 16));
+      *reinterpret_cast<uint2*>(dst + (size_t)d * B + ch * 4) = val;
+    }
+  }
+  if (g.need8 || g.need4) {
+    uint8_t* dst = w.vt_fp8 + ((size_t)bh * g.Nb + b) * (size_t)D * kp8;
+    const int per_row = kp8 / 8;
+    for (int i = tid; i < D * per_row; i += kThreads) {
+      const int d = i / per_row, ch = i - (i / per_row) * per_row;
+      const uint8_t* s = &s_vt8[d][ch * 8];
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo |= (uint32_t)s[j] << (8 * j);
+        hi |= (uint32_t)s[4 + j] << (8 * j);
+      }
+      *reinterpret_cast<uint2*>(dst + (size_t)d * kp8 + ch * 8) = make_uint2(lo, hi);
+    }
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+template <int D>
+hipError_t prepare_d(const Geo& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const Ws& w, hipStream_t s) {
+  prep_qk_kernel<D><<<dim3(g.Nb, g.bh, 2), kThreads, 0, s>>>(g, q, k, w);
+  const size_t na = (size_t)g.bh * D;
+  fill_u32_kernel<<<(unsigned)((na + 255) / 256), 256, 0, s>>>(w.v_amax, na, 0u);
+  const int slice = 2048;
+  const int slices = (g.N + slice - 1) / slice;
+  v_amax_kernel<D><<<dim3(slices, g.bh), kThreads, 0, s>>>(g, v, w.v_amax, slice);
+  v_pack_kernel<D><<<dim3(g.Nb, g.bh), kThreads, 0, s>>>(g, v, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const Geo& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const Ws& w, hipStream_t s) {
+  return g.D == 64 ? prepare_d<64>(g, q, k, v, w, s) : prepare_d<128>(g, q, k, v, w, s);
+}
+
+}  // namespace dap

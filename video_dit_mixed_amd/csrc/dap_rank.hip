@@ -1,0 +1,226 @@
+// Per-head ranking of all region pairs and 4-level block assignment (gfx950).
+//
+// Method: "DraftAttention2" -- pchao.org blog, section 方法概览 bullet 2 (within each head all region
+// pairs are sorted by draft score; by quota they get 16-bit, then INT8, then 4-bit; the rest are
+// skipped; rows may differ in count and mix under the head budget); newx.sg paper card, AI Summary
+// (a shared sorting mechanism).
+//
+// Only the three cut keys are needed, not a full sort: the pair at rank c-1 for c in (c16, c8, c4).
+// Keys are 87-bit integers, ascending key = (score descending, pair index ascending):
+//   key = ((~bits(score) & 0x7fff'ffff'ffff'ffff) << 24) | (qb*Nb + kb)
+// (scores are >= 0, so their IEEE bit patterns are ordered).  An MSD radix select finds each cut
+// key exactly in 8 digit passes (7 x 11 bits + 10 bits); each pass is a histogram over all pairs
+// whose key shares the cut's known prefix (LDS histograms, flushed with integer atomics, so the
+// result does not depend on scheduling), then a one-workgroup scan per head picks the digit.
+// Finally one wave per query row classifies its pairs against the cut keys, writes the uint8 map
+// and the per-level key-block lists (ascending kb) with ballot/popcount compaction.
+#include "dap_internal.h"
+
+namespace dap {
+namespace {
+
+typedef unsigned __int128 u128;
+
+__device__ __forceinline__ u128 pair_key(double score, uint32_t idx) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(score);
+  const unsigned long long hi = (~u) & 0x7fffffffffffffffull;
+  return ((u128)hi << 24) | (u128)idx;
+}
+
+__device__ __forceinline__ u128 make_u128(unsigned long long hi, unsigned long long lo) {
+  return ((u128)hi << 64) | (u128)lo;
+}
+
+__global__ void rank_init_kernel(Geo g, RankCut* st, uint32_t* hist) {
+  const int bh = blockIdx.x;
+  const long long cuts[3] = {g.c16, g.c8, g.c4};
+  if (threadIdx.x < 3) {
+    const long long c = cuts[threadIdx.x];
+    RankCut r;
+    r.prefix_hi = 0;
+    r.prefix_lo = 0;
+    r.remaining = c - 1;
+    r.mode = c == 0 ? kCutNone : (c == g.pairs ? kCutAll : kCutKey);
+    r.pad = 0;
+    st[bh * 3 + threadIdx.x] = r;
+  }
+  for (int i = threadIdx.x; i < 3 * kRankBins; i += blockDim.x) hist[(size_t)bh * 3 * kRankBins + i] = 0;
+}
+
+constexpr int kHistThreads = 256;
+constexpr int kPerThread = 64;
+constexpr int kChunk = kHistThreads * kPerThread;
+
+__global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(Geo g, const double* __restrict__ scores,
+                                                                 const RankCut* __restrict__ st,
+                                                                 uint32_t* __restrict__ hist, int pass) {
+  __shared__ uint32_t s_h[3][kRankBins];
+  const int bh = blockIdx.y;
+  bool active[3];
+  u128 prefix[3];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const RankCut c = st[bh * 3 + j];
+    active[j] = c.mode == kCutKey;
+    prefix[j] = make_u128(c.prefix_hi, c.prefix_lo);
+    any |= active[j];
+  }
+  if (!any) return;
+  for (int i = threadIdx.x; i < 3 * kRankBins; i += kHistThreads) (&s_h[0][0])[i] = 0;
+  __syncthreads();
+  const int shift = rank_digit_shift(pass);
+  const int top = shift + rank_digit_width(pass);
+  const uint32_t mask = (1u << rank_digit_width(pass)) - 1u;
+  const double* sc = scores + (size_t)bh * g.pairs;
+  const long long i0 = (long long)blockIdx.x * kChunk;
+  const long long i1 = min((long long)g.pairs, i0 + kChunk);
+  for (long long i = i0 + threadIdx.x; i < i1; i += kHistThreads) {
+    const u128 key = pair_key(sc[i], (uint32_t)i);
+    const u128 hi = key >> top;
+    const uint32_t digit = (uint32_t)(key >> shift) & mask;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (active[j] && hi == prefix[j]) atomicAdd(&s_h[j][digit], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = hist + (size_t)bh * 3 * kRankBins;
+  for (int i = threadIdx.x; i < 3 * kRankBins; i += kHistThreads) {
+    const uint32_t v = (&s_h[0][0])[i];
+    if (v) atomicAdd(&gh[i], v);
+  }
+}
+
+// One workgroup per head: choose the digit of each active cut and clear the histograms.
+__global__ __launch_bounds__(256) void rank_select_kernel(RankCut* st, uint32_t* hist, int pass) {
+  __shared__ unsigned long long s_scan[256];
+  __shared__ int s_digit;
+  __shared__ long long s_rem;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  constexpr int per = kRankBins / 256;  // 8 bins per thread
+  const int width = rank_digit_width(pass);
+  for (int j = 0; j < 3; ++j) {
+    RankCut c = st[bh * 3 + j];  // uniform
+    uint32_t* h = hist + ((size_t)bh * 3 + j) * kRankBins;
+    if (c.mode == kCutKey) {
+      unsigned long long cnt[per];
+      unsigned long long tsum = 0;
+#pragma unroll
+      for (int b = 0; b < per; ++b) {
+        cnt[b] = h[tid * per + b];
+        tsum += cnt[b];
+      }
+      s_scan[tid] = tsum;
+      __syncthreads();
+      // inclusive Hillis-Steele scan over 256 thread sums
+      for (int o = 1; o < 256; o <<= 1) {
+        const unsigned long long add = tid >= o ? s_scan[tid - o] : 0ull;
+        __syncthreads();
+        s_scan[tid] += add;
+        __syncthreads();
+      }
+      const unsigned long long base = s_scan[tid] - tsum;
+      const long long t = c.remaining;
+      if ((long long)base <= t && t < (long long)(base + tsum)) {
+        unsigned long long cum = base;
+#pragma unroll
+        for (int b = 0; b < per; ++b) {
+          if ((long long)(cum + cnt[b]) > t) {
+            s_digit = tid * per + b;
+            s_rem = t - (long long)cum;
+            break;
+          }
+          cum += cnt[b];
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        u128 p = make_u128(c.prefix_hi, c.prefix_lo);
+        p = (p << width) | (u128)(uint32_t)s_digit;
+        c.prefix_hi = (unsigned long long)(p >> 64);
+        c.prefix_lo = (unsigned long long)p;
+        c.remaining = s_rem;
+        st[bh * 3 + j] = c;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int b = 0; b < per; ++b) h[tid * per + b] = 0;
+  }
+}
+
+// One wave per query row: level of each pair, uint8 map, per-level ascending kb lists, counts.
+__global__ __launch_bounds__(256) void rank_assign_kernel(Geo g, const double* __restrict__ scores,
+                                                         const RankCut* __restrict__ st, uint8_t* __restrict__ map,
+                                                         uint16_t* __restrict__ lists, int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int qb = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int bh = blockIdx.y;
+  if (qb >= g.Nb) return;
+  int mode[3];
+  u128 cut[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const RankCut c = st[bh * 3 + j];
+    mode[j] = c.mode;
+    cut[j] = make_u128(c.prefix_hi, c.prefix_lo);
+  }
+  const int Nb = g.Nb;
+  const size_t rowoff = (size_t)bh * g.pairs + (size_t)qb * Nb;
+  const double* sc = scores + rowoff;
+  auto level_of = [&](int kb) -> int {
+    const u128 key = pair_key(sc[kb], (uint32_t)((size_t)qb * Nb + kb));
+    int lv = 0;
+#pragma unroll
+    for (int j = 2; j >= 0; --j) {  // j = 0: 16-bit cut, 1: 8-bit, 2: 4-bit
+      const bool in = mode[j] == kCutAll || (mode[j] == kCutKey && key <= cut[j]);
+      if (in) lv = 3 - j;
+    }
+    return lv;
+  };
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int n[4] = {0, 0, 0, 0};
+  for (int kb0 = 0; kb0 < Nb; kb0 += 64) {
+    const int kb = kb0 + lane;
+    const int lv = kb < Nb ? level_of(kb) : -1;
+    if (kb < Nb) map[rowoff + kb] = (uint8_t)lv;
+#pragma unroll
+    for (int L = 1; L <= 3; ++L) n[L] += __popcll(__ballot(lv == L));
+  }
+  uint16_t* lst = lists + rowoff;
+  int base[4] = {0, n[3] + n[2], n[3], 0};  // offsets of the 4-bit, 8-bit, 16-bit lists
+  for (int kb0 = 0; kb0 < Nb; kb0 += 64) {
+    const int kb = kb0 + lane;
+    const int lv = kb < Nb ? level_of(kb) : -1;
+#pragma unroll
+    for (int L = 1; L <= 3; ++L) {
+      const unsigned long long m = __ballot(lv == L);
+      if (lv == L) lst[base[L] + __popcll(m & below)] = (uint16_t)kb;
+      base[L] += __popcll(m);
+    }
+  }
+  if (lane == 0) {
+    int32_t* cnt = counts + ((size_t)bh * Nb + qb) * 4;
+    cnt[0] = n[3];
+    cnt[1] = n[2];
+    cnt[2] = n[1];
+    cnt[3] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rank(const Geo& g, const Ws& w, hipStream_t s) {
+  RankCut* st = static_cast<RankCut*>(w.rank_state);
+  rank_init_kernel<<<g.bh, 256, 0, s>>>(g, st, w.rank_hist);
+  const unsigned chunks = (unsigned)((g.pairs + kChunk - 1) / kChunk);
+  for (int pass = 0; pass < kRankDigits; ++pass) {
+    rank_hist_kernel<<<dim3(chunks, g.bh), kHistThreads, 0, s>>>(g, w.scores, st, w.rank_hist, pass);
+    rank_select_kernel<<<g.bh, 256, 0, s>>>(st, w.rank_hist, pass);
+  }
+  rank_assign_kernel<<<dim3((g.Nb + 3) / 4, g.bh), 256, 0, s>>>(g, w.scores, st, w.map, w.lists,
+                                                                   w.counts);
+  return hipGetLastError();
+}
+
+}  // namespace dap

@@ -1,0 +1,45 @@
+// Restore (gfx950): packed attention output [bh][Np][D] -> [batch, heads, N, D] in the original
+// token order, pad rows dropped.
+//
+// Method: pith.science, "DraftAttention: Fast Video Diffusion via Low-Resolution Attention
+// Guidance", Abstract (the reordered sequence is attended and then put back in its original
+// order).  One thread per 16-byte chunk of the output: writes are fully coalesced, reads are
+// contiguous within each region row.
+#include "dap_internal.h"
+
+namespace dap {
+namespace {
+
+__global__ __launch_bounds__(256) void restore_kernel(Geo g, const uint16_t* __restrict__ packed,
+                                                      uint16_t* __restrict__ out) {
+  const int CH = g.D / 8;
+  const size_t total = (size_t)g.bh * g.N * CH;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t tok = i / CH;
+    const int c = (int)(i - tok * CH);
+    const int bh = (int)(tok / g.N);
+    const int n = (int)(tok - (size_t)bh * g.N);
+    const int hw = g.H * g.W;
+    const int t = n / hw;
+    const int yx = n - t * hw;
+    const int y = yx / g.W, x = yx - (yx / g.W) * g.W;
+    const int ry = y / g.rh, iy = y - ry * g.rh;
+    const int rx = x / g.rw, ix = x - rx * g.rw;
+    const size_t b = ((size_t)t * g.nby + ry) * g.nbx + rx;
+    const size_t p = b * g.B + (size_t)iy * g.rw + ix;
+    const uint4 v = *reinterpret_cast<const uint4*>(packed + ((size_t)bh * g.Np + p) * g.D + c * 8);
+    *reinterpret_cast<uint4*>(out + tok * g.D + c * 8) = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_restore(const Geo& g, const Ws& w, uint16_t* out, hipStream_t s) {
+  const size_t total = (size_t)g.bh * g.N * (g.D / 8);
+  const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 * 4 ? (total + 255) / 256 : 65536 * 4);
+  restore_kernel<<<blocks, 256, 0, s>>>(g, w.out, out);
+  return hipGetLastError();
+}
+
+}  // namespace dap
