@@ -98,6 +98,9 @@ typedef struct {
  *   lists           [bh][Nb][Nb] uint16: per query block, key blocks of level 16, then 8, then 4,
  *                   each ascending
  *   counts          [bh][Nb][4] int32: n16, n8, n4, 0
+ *   zeros           256 zero bytes (source of the all-zero key rows a 16-token block pads to)
+ *   order           [8][bh * ceil(Nb/8)] uint32 (bh << 16 | qb): attention work order, one slice per
+ *                   accelerator die (XCD) -- rows with similar key lists share a slice
  *   out             [bh][Np][D] bf16 attention output in packed order */
 typedef struct {
   int32_t Hp, Wp, nby, nbx, Nb, B, Np, kp8, bh, D;
@@ -108,7 +111,7 @@ typedef struct {
   uint64_t off_vt_fp8, off_v_scale, off_v_amax;
   uint64_t off_q_avg, off_q_max, off_k_avg, off_k_max;
   uint64_t off_scores, off_lmax, off_rank_state, off_rank_hist;
-  uint64_t off_map, off_lists, off_counts, off_out;
+  uint64_t off_map, off_lists, off_counts, off_out, off_zeros, off_order;
   uint64_t total_bytes;
 } dap_layout;
 

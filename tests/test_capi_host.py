@@ -95,7 +95,8 @@ def _layout_py(w):
              ("q_avg", bh * Nb * D * 8), ("q_max", bh * Nb * D * 8), ("k_avg", bh * Nb * D * 8),
              ("k_max", bh * Nb * D * 8), ("scores", bh * Nb * Nb * 8), ("lmax", bh * Nb * Nb * 8),
              ("rank_state", bh * 3 * 32), ("rank_hist", bh * 3 * 2048 * 4), ("map", bh * Nb * Nb),
-             ("lists", bh * Nb * Nb * 2), ("counts", bh * Nb * 16), ("out", bh * Np * D * 2)]
+             ("lists", bh * Nb * Nb * 2), ("counts", bh * Nb * 16), ("out", bh * Np * D * 2),
+             ("zeros", 256), ("order", 8 * bh * -(-Nb // 8) * 4)]
     off, o = {}, 0
     for name, n in sizes:
         off["off_" + name] = o

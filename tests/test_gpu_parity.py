@@ -155,7 +155,26 @@ def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None):
         _check_out(S, r, blocks)
         packed.append((bhi, S.out_packed))
     _check_restore(out, packed, L, w)
+    _check_order(ws, L)
     return ws, out
+
+
+def _check_order(ws, L):
+    """The attention work order covers every (head, query block) exactly once, each die's slice
+    holding a contiguous share of every head."""
+    import torch
+    Nb, BH = L["Nb"], L["bh"]
+    stride = BH * -(-Nb // 8)
+    tab = b.section(ws, L, "order", torch.int32, (8, stride)).cpu().numpy().view(np.uint32)
+    seen = []
+    for x in range(8):
+        size = (x + 1) * Nb // 8 - x * Nb // 8
+        items = tab[x, :BH * size]
+        assert np.all((items >> 16).reshape(BH, size) == np.arange(BH)[:, None])
+        seen.append(items)
+    allitems = np.sort(np.concatenate(seen))
+    exp = np.sort((np.arange(BH)[:, None].astype(np.uint32) << 16 | np.arange(Nb)[None, :]).ravel())
+    np.testing.assert_array_equal(allitems, exp)
 
 
 # ------------------------------------------------------------------------------------ workloads

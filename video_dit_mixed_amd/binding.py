@@ -41,7 +41,7 @@ _LAYOUT_INT64 = ["pairs", "c16", "c8", "c4"]
 _LAYOUT_OFFS = ["q_bf16", "k_bf16", "vt_bf16", "q_i8", "k_i8", "q_i8_scale", "k_i8_scale",
                 "q_fp4", "k_fp4", "q_e8m0", "k_e8m0", "vt_fp8", "v_scale", "v_amax",
                 "q_avg", "q_max", "k_avg", "k_max", "scores", "lmax", "rank_state", "rank_hist",
-                "map", "lists", "counts", "out"]
+                "map", "lists", "counts", "out", "zeros", "order"]
 
 
 class _Layout(ctypes.Structure):

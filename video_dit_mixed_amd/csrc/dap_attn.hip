@@ -18,9 +18,11 @@
 //         16-bit: bf16(P) x bf16 V        low-bit: e4m3(2^8 P) x e4m3 V (scaled f8f6f4 MFMA)
 // One fp32 accumulator serves all phases.  At the first low-bit block its channel d is converted
 // to low-bit units (x 2^8 / s_V[d]); the end multiplies by s_V[d] 2^-8 and divides by l.
-// Key and V tiles are staged through LDS with 16-byte-staggered rows (bank-conflict-free reads);
-// the matrix-core operand orders were fixed when the operands were packed, so every LDS read is
-// one or two 16-byte loads per lane.
+// Key and V tiles are staged through LDS in an XOR-swizzled layout (bank-conflict-free reads).
+// Global loads run ahead in registers: a tile's V loads are issued before its Q K^T and stored to
+// LDS just before its P V; the next tile's K loads are issued before the P V products and stored
+// at the top of the next iteration.  The matrix-core operand
+// orders were fixed when the operands were packed, so every LDS read is one or two 16-byte loads.
 #include "dap_internal.h"
 
 namespace dap {
@@ -43,15 +45,38 @@ struct AttnCfg {
   static constexpr int MT = KT / 32;               // S^T m-tiles (32 keys each)
   static constexpr int DT = D / 32;                // O^T m-tiles (32 channels each)
   static constexpr int KP8 = (B + 63) / 64 * 64;   // FP8 V^T row length
-  static constexpr int KSTR16 = 2 * D + 16;        // LDS row strides (bytes)
-  static constexpr int KSTR8 = D + 16;
-  static constexpr int KSTR4 = D / 2 + 16;
-  static constexpr int VSTR16 = 2 * B + 16;
-  static constexpr int VSTR8 = KP8 + 16;
-  static constexpr int KBYTES = KT * KSTR16;
-  static constexpr int VBYTES = (D * VSTR16 > D * VSTR8) ? D * VSTR16 : D * VSTR8;
-  static constexpr int SBYTES = KT * (D / 32);
+  static constexpr int KBYTES = KT * 2 * D;        // largest key tile (bf16)
+  static constexpr int SBYTES = 64 * NW * 4;       // E8M0 key scales (one 4-byte DMA per wave)
+  static constexpr int VBYTES = (D * 2 * B > D * KP8) ? D * 2 * B : D * KP8;
 };
+
+// Per-phase tile geometry.  PH = 0: bf16 K rows / bf16 V^T rows; 1: int8 K / e4m3 V^T;
+// 2: E2M1 K (+ E8M0 scales) / e4m3 V^T.
+template <int B, int D, int PH>
+struct PhaseCfg {
+  using C = AttnCfg<B, D>;
+  static constexpr int KRB = PH == 0 ? 2 * D : (PH == 1 ? D : D / 2);  // key row bytes
+  static constexpr int KRC = KRB / 16;                                 // 16-byte chunks per row
+  static constexpr int VRB = PH == 0 ? 2 * B : C::KP8;                 // V^T row bytes
+  static constexpr int VRC = VRB / 16;
+  static_assert(KRC <= 16 && VRC <= 16, "rows up to 256 bytes");
+};
+
+// LDS tiles are stored unpadded with the 16-byte chunks of each row XOR-swizzled so that the
+// 16-lane groups of a ds_read_b128 (32 consecutive rows, one chunk each) hit distinct banks:
+// physical chunk = logical chunk ^ ((row / (16 / RC)) % RC) for rows of RC chunks.
+template <int RC>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((row / (16 / RC)) % RC);
+}
+// Rows 32*m + n share the swizzle of row n (32 is a multiple of 16/RC * RC), so an operand read
+// is a per-lane offset plus a compile-time row-tile offset.
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -63,54 +88,48 @@ struct RowCtx {
   const uint16_t* list;   // key-block list of the row
 };
 
-// Copy ROWS rows of CPR 16-byte chunks from global (row stride GS bytes) to LDS (row stride LS
-// bytes) with NT threads; rows >= valid are written as zeros.  Every thread keeps one global and
-// one LDS base address; the per-pass offsets are compile-time constants.
-template <int ROWS, int CPR, int NT, int GS, int LS>
-__device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ gsrc, uint8_t* ldst, int tid,
-                                          int valid) {
-  constexpr int RPP = NT / CPR;
-  constexpr int PASSES = (ROWS + RPP - 1) / RPP;
-  const int r0 = tid / CPR, cc = tid - (tid / CPR) * CPR;
-  const uint8_t* gp = gsrc + (size_t)r0 * GS + cc * 16;
-  uint8_t* lp = ldst + r0 * LS + cc * 16;
-  uint4 v[PASSES];
+// One key block's operand tile held in registers between its global load and its LDS store.
+// Slot s (16 bytes) of a tile of rows with RC chunks sits at LDS byte 16*s and holds row s / RC,
+// logical chunk (s % RC) ^ swizzle; thread t owns slots t, t + NT, t + 2*NT, ...
+template <int ROWS, int RC, int NT>
+struct TileRegs {
+  static constexpr int N = ROWS * RC / NT;
+  static_assert(ROWS * RC % NT == 0, "tile must split evenly over the threads");
+  uint4 v[N];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ gsrc, int valid, int tid) {
 #pragma unroll
-  for (int j = 0; j < PASSES; ++j) {
-    const int r = r0 + j * RPP;
-    v[j] = (r < ROWS && r < valid) ? *reinterpret_cast<const uint4*>(gp + (size_t)j * RPP * GS)
-                                   : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < N; ++j) {
+      const int sl = tid + j * NT;
+      const int r = sl / RC, pc = sl - (sl / RC) * RC;
+      v[j] = r < valid ? *reinterpret_cast<const uint4*>(gsrc + (size_t)r * (RC * 16) + 16 * swz<RC>(r, pc))
+                       : make_uint4(0, 0, 0, 0);
+    }
   }
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
 #pragma unroll
-  for (int j = 0; j < PASSES; ++j)
-    if (r0 + j * RPP < ROWS) *reinterpret_cast<uint4*>(lp + j * RPP * LS) = v[j];
+    for (int j = 0; j < N; ++j) *reinterpret_cast<uint4*>(lds + 16 * (tid + j * NT)) = v[j];
+  }
+};
+
+// Workgroup barrier without a memory fence (LDS traffic is ordered by lgkmcnt; global loads that
+// are still in flight belong to the next tile and must not be waited for here).
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int B, int D, int PH>
+__device__ __forceinline__ const uint8_t* k_tile_src(const Geo& g, const Ws& w, int bh, int kb) {
+  const size_t krow0 = (size_t)bh * g.Np + (size_t)kb * B;
+  return PH == 0 ? reinterpret_cast<const uint8_t*>(w.k_bf16 + krow0 * D)
+       : PH == 1 ? reinterpret_cast<const uint8_t*>(w.k_i8 + krow0 * D)
+                 : w.k_fp4 + krow0 * (D / 2);
 }
 
-template <int B, int D>
-__device__ __forceinline__ void stage_tile(const Geo& g, const Ws& w, const RowCtx& c, int phase,
-                                           int kb, uint8_t* sK, uint8_t* sV, uint8_t* sKs) {
+template <int B, int D, int PH>
+__device__ __forceinline__ const uint8_t* v_tile_src(const Geo& g, const Ws& w, int bh, int kb) {
   using C = AttnCfg<B, D>;
-  const size_t krow0 = (size_t)c.bh * g.Np + (size_t)kb * B;
-  const int tid = c.tid;
-  if (phase == 0) {
-    copy_rows<C::KT, 2 * D / 16, C::NT, 2 * D, C::KSTR16>(
-        reinterpret_cast<const uint8_t*>(w.k_bf16 + krow0 * D), sK, tid, B);
-    copy_rows<D, 2 * B / 16, C::NT, 2 * B, C::VSTR16>(
-        reinterpret_cast<const uint8_t*>(w.vt_bf16 + ((size_t)c.bh * g.Nb + kb) * (size_t)D * B), sV,
-        tid, D);
-    return;
-  }
-  if (phase == 1) {
-    copy_rows<C::KT, D / 16, C::NT, D, C::KSTR8>(
-        reinterpret_cast<const uint8_t*>(w.k_i8 + krow0 * D), sK, tid, B);
-  } else {
-    copy_rows<C::KT, D / 32, C::NT, D / 2, C::KSTR4>(w.k_fp4 + krow0 * (D / 2), sK, tid, B);
-    const uint8_t* esrc = w.k_e8m0 + krow0 * (D / 32);
-    for (int i = tid; i < C::KT * (D / 32); i += C::NT)
-      sKs[i] = i < B * (D / 32) ? esrc[i] : (uint8_t)127;
-  }
-  copy_rows<D, C::KP8 / 16, C::NT, C::KP8, C::VSTR8>(
-      w.vt_fp8 + ((size_t)c.bh * g.Nb + kb) * (size_t)D * C::KP8, sV, tid, D);
+  return PH == 0
+             ? reinterpret_cast<const uint8_t*>(w.vt_bf16 + ((size_t)bh * g.Nb + kb) * (size_t)D * B)
+             : w.vt_fp8 + ((size_t)bh * g.Nb + kb) * (size_t)D * C::KP8;
 }
 
 // All key blocks of one precision phase (PH = 0: 16-bit, 1: 8-bit, 2: 4-bit) for this row.
@@ -139,55 +158,79 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     qsc[ks] = (PH == 2 && c.qok) ? (int)w.q_e8m0[c.qrow * (D / 32) + 2 * ks + gh] : 127;
   }
   if (PH == 1) s_q = w.q_i8_scale[(size_t)c.bh * g.Nb + c.qb];
+  using P = PhaseCfg<B, D, PH>;
+  const int lane = c.tid & 63;
+  TileRegs<C::KT, P::KRC, C::NT> kreg;
+  TileRegs<D, P::VRC, C::NT> vreg;
+  uint32_t kscale = 0;  // E8M0 key scales of the staged tile (4-bit phase), 4 bytes per thread
+
+  // prologue: the first key block's tiles go to registers
+  {
+    const int kb0 = __builtin_amdgcn_readfirstlane(c.list[off]);
+    kreg.load(k_tile_src<B, D, PH>(g, w, c.bh, kb0), B, c.tid);
+    if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
+      kscale = c.tid < B * (D / 32) / 4
+                   ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb0 * B) * (D / 32) + 4 * c.tid)
+                   : 0x7f7f7f7fu;
+  }
 
   for (int it = 0; it < np; ++it) {
-    const int kb = c.list[off + it];
+    const int kb = __builtin_amdgcn_readfirstlane(c.list[off + it]);
+    const int kb_next = it + 1 < np ? __builtin_amdgcn_readfirstlane(c.list[off + it + 1]) : kb;
     // real extent of key block kb (regions at the high-y / high-x edge hold padding)
     const int per = g.nby * g.nbx;
     const int rem = kb % per;
     const int ry = rem / g.nbx, rx = rem - ry * g.nbx;
     const int vh = min(g.rh, g.H - ry * g.rh), vw = min(g.rw, g.W - rx * g.rw);
     const bool full = vh == g.rh && vw == g.rw && B == C::KT;
-    __syncthreads();  // previous tile fully consumed
-    stage_tile<B, D>(g, w, c, PH, kb, sK, sV, sKs);
+    bar();  // every wave is done with the previous tile's sK / sV / sBias
+    kreg.store(sK, c.tid);
+    // this tile's V streams into registers while Q K^T and the softmax run
+    vreg.load(v_tile_src<B, D, PH>(g, w, c.bh, kb), D, c.tid);
+    if (PH == 2 && c.tid < C::KT * (D / 32) / 4) *reinterpret_cast<uint32_t*>(sKs + 4 * c.tid) = kscale;
     if (!full && c.tid < C::KT) {
       const int m = c.tid, iy = m / g.rw, ix = m - (m / g.rw) * g.rw;
       sBias[m] = (m < B && iy < vh && ix < vw) ? 0.0f : -INFINITY;
     }
-    __syncthreads();
+    bar();
+    // per-lane LDS addresses are recomputed in every iteration (a few integer ops) instead of
+    // being hoisted out of the loop, where they would pin dozens of registers
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int nl = ln & 31, gl = ln >> 5;
 
     // ---- S^T = K Q^T
     f32x16 S[C::MT];
     float c_scale = kLog2e * inv_sqrt_d;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
-      const int krow = 32 * mt + n;
       if (PH == 0) {
         f32x16 acc = {};
-        const uint8_t* rowp = sK + krow * C::KSTR16 + 16 * gh;
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lds16(rowp + 32 * ks)),
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, lds16(sK + 32 * mt * P::KRB + nl * P::KRB +
+                                               16 * swz<P::KRC>(nl, 2 * ks + gl))),
                                                         __builtin_bit_cast(bf16x8, qop[ks]), acc, 0, 0, 0);
         S[mt] = acc;
       } else if (PH == 1) {
         i32x16 acc = {};
-        const uint8_t* rowp = sK + krow * C::KSTR8 + 16 * gh;
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks)
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, lds16(rowp + 32 * ks)),
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              __builtin_bit_cast(i32x4, lds16(sK + 32 * mt * P::KRB + nl * P::KRB +
+                                              16 * swz<P::KRC>(nl, 2 * ks + gl))),
                                                       __builtin_bit_cast(i32x4, qop[ks]), acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[mt][r] = (float)acc[r];
       } else {
         f32x16 acc = {};
-        const uint8_t* rowp = sK + krow * C::KSTR4 + 16 * gh;
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) {
-          const uint4 u = lds16(rowp + 32 * ks);
+          const uint4 u = lds16(sK + 32 * mt * P::KRB + nl * P::KRB + 16 * swz<P::KRC>(nl, 2 * ks + gl));
           const i32x8 a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
           const i32x8 b = {(int)qop[ks].x, (int)qop[ks].y, (int)qop[ks].z, (int)qop[ks].w, 0, 0, 0, 0};
-          const int ksc = (int)sKs[krow * (D / 32) + 2 * ks + gh];
+          const int ksc = (int)sKs[(32 * mt + nl) * (D / 32) + 2 * ks + gl];
           acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, 0, ksc, 0, qsc[ks]);
         }
         S[mt] = acc;
@@ -196,12 +239,17 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     }
     if (PH == 1) c_scale = s_q * w.k_i8_scale[(size_t)c.bh * g.Nb + kb] * (kLog2e * inv_sqrt_d);
 
-    // ---- scale to the log2 domain; pad keys (and key slots beyond B) get -inf from sBias
+    // ---- online softmax in the log2 domain, one running-max update per key block.
+    // Full blocks: the tile max is taken on the raw scores and scaled once (c_scale > 0 keeps the
+    // order; c_scale = 0 gives 0 either way), and the scale folds into the exponent's FMA.
+    // Edge blocks: scores are scaled and pad keys set to -inf from sBias first.
+    float mx = -INFINITY;
     if (full) {
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[mt][r] *= c_scale;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_scale;
     } else {
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
@@ -213,26 +261,36 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
           S[mt][4 * r4 + 2] = S[mt][4 * r4 + 2] * c_scale + bias4.z;
           S[mt][4 * r4 + 3] = S[mt][4 * r4 + 3] * c_scale + bias4.w;
         }
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
     }
-
-    // ---- online softmax (log2 domain), one running-max update per key block
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float bias = PH == 0 ? m_new : m_new - 8.0f;  // low-bit phases produce 2^8 P
+    const float nbias = PH == 0 ? -m_new : 8.0f - m_new;  // low-bit phases produce 2^8 P
+    const float cs = full ? c_scale : 1.0f;
+    // P goes straight into the packed B-operand registers of the P.V products
+    uint32_t pk[C::MT][PH == 0 ? 8 : 4];
     float psum = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(S[mt][r] - bias);
-        S[mt][r] = p;
-        psum += p;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(fmaf(S[mt][4 * r4 + e], cs, nbias));
+          psum += p[e];
+        }
+        if (PH == 0) {
+          pk[mt][2 * r4] = pack_bf16(p[0], p[1]);
+          pk[mt][2 * r4 + 1] = pack_bf16(p[2], p[3]);
+        } else {
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          pk[mt][r4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+        }
       }
     if (PH != 0) psum *= 0.00390625f;  // 2^-8, exact
     l_run = alpha * l_run + psum;
@@ -244,18 +302,28 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T.  V goes to LDS first; the next key block's K streams into registers
+    // during the products (the load is unconditional -- the last tile re-reads its own block --
+    // so the staging registers are dead between the store at the top and this point; the
+    // scheduling barrier keeps it from being hoisted into the softmax)
+    vreg.store(sV, c.tid);
+    bar();
+    __builtin_amdgcn_sched_barrier(0);
+    kreg.load(k_tile_src<B, D, PH>(g, w, c.bh, kb_next), B, c.tid);
+    if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
+      kscale = c.tid < B * (D / 32) / 4
+                   ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb_next * B) * (D / 32) + 4 * c.tid)
+                   : 0x7f7f7f7fu;
     if (PH == 0) {
 #pragma unroll
       for (int c16 = 0; c16 < B / 16; ++c16) {
-        const int mt = c16 >> 1, rb = 8 * (c16 & 1);
-        bf16x8 bop;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bop[j] = (__bf16)S[mt][rb + j];
+        const int mt = c16 >> 1, wb = 4 * (c16 & 1);
+        const bf16x8 bop = __builtin_bit_cast(
+            bf16x8, make_uint4(pk[mt][wb], pk[mt][wb + 1], pk[mt][wb + 2], pk[mt][wb + 3]));
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const bf16x8 a = __builtin_bit_cast(
-              bf16x8, lds16(sV + (32 * dt + n) * C::VSTR16 + (16 * c16 + 8 * gh) * 2));
+              bf16x8, lds16(sV + 32 * dt * P::VRB + nl * P::VRB + 16 * swz<P::VRC>(nl, 2 * c16 + gl)));
           O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, O[dt], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -268,19 +336,13 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         for (int hsel = 0; hsel < 2; ++hsel) {
           const int mt = 2 * c64 + hsel;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            int word = 0;
-            if (mt < C::MT) {
-              word = __builtin_amdgcn_cvt_pk_fp8_f32(S[mt][4 * q4 + 0], S[mt][4 * q4 + 1], word, false);
-              word = __builtin_amdgcn_cvt_pk_fp8_f32(S[mt][4 * q4 + 2], S[mt][4 * q4 + 3], word, true);
-            }
-            bop[4 * hsel + q4] = word;
-          }
+          for (int q4 = 0; q4 < 4; ++q4) bop[4 * hsel + q4] = mt < C::MT ? (int)pk[mt < C::MT ? mt : 0][q4] : 0;
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const uint8_t* vp = sV + (32 * dt + n) * C::VSTR8 + 64 * c64 + 32 * gh;
-          const uint4 u0 = lds16(vp), u1 = lds16(vp + 16);
+          const uint8_t* vp = sV + 32 * dt * P::VRB + nl * P::VRB;
+          const uint4 u0 = lds16(vp + 16 * swz<P::VRC>(nl, 4 * c64 + 2 * gl));
+          const uint4 u1 = lds16(vp + 16 * swz<P::VRC>(nl, 4 * c64 + 2 * gl + 1));
           const i32x8 a = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
                            (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
           O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, O[dt], 0, 0, 0, kScaleOne,
@@ -298,13 +360,20 @@ void attn_kernel(Geo g, Ws w) {
   using C = AttnCfg<B, D>;
   __shared__ __attribute__((aligned(16))) uint8_t sK[C::KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sV[C::VBYTES];
-  __shared__ uint8_t sKs[C::SBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sKs[C::SBYTES];
   __shared__ __attribute__((aligned(16))) float sBias[C::KT];
 
+  // Workgroups are dispatched round-robin over the 8 dies: workgroup id x + 8j runs on die x and
+  // takes entry j of that die's slice of the work order.
   RowCtx c;
   const int Nb = g.Nb;
-  c.bh = blockIdx.x / Nb;
-  c.qb = blockIdx.x - c.bh * Nb;
+  {
+    const int x = blockIdx.x & (kXcds - 1), j = blockIdx.x / kXcds;
+    if (j >= g.bh * xcd_chunk_size(x, Nb)) return;
+    const uint32_t item = w.order[(size_t)x * xcd_stride(g.bh, Nb) + j];
+    c.bh = (int)(item >> 16);
+    c.qb = (int)(item & 0xffff);
+  }
   c.tid = threadIdx.x;
   const int wv = c.tid >> 6, lane = c.tid & 63;
   c.n = lane & 31;
@@ -372,7 +441,7 @@ void attn_kernel(Geo g, Ws w) {
 template <int B, int D>
 hipError_t attn_bd(const Geo& g, const Ws& w, hipStream_t s) {
   using C = AttnCfg<B, D>;
-  attn_kernel<B, D><<<(unsigned)(g.bh * g.Nb), C::NT, 0, s>>>(g, w);
+  attn_kernel<B, D><<<(unsigned)(kXcds * xcd_stride(g.bh, g.Nb)), C::NT, 0, s>>>(g, w);
   return hipGetLastError();
 }
 

@@ -117,6 +117,8 @@ void make_layout(const Geo& g, dap_layout* L) {
   L->off_lists = take(bh * Nb * Nb * 2);
   L->off_counts = take(bh * Nb * 4 * 4);
   L->off_out = take(bh * Np * D * 2);
+  L->off_zeros = take(256);
+  L->off_order = take((uint64_t)dap::kXcds * dap::xcd_stride(g.bh, g.Nb) * 4);
   L->total_bytes = o;
 }
 
@@ -149,6 +151,8 @@ Ws make_ws(void* base, const dap_layout& L) {
   w.lists = reinterpret_cast<uint16_t*>(b + L.off_lists);
   w.counts = reinterpret_cast<int32_t*>(b + L.off_counts);
   w.out = reinterpret_cast<uint16_t*>(b + L.off_out);
+  w.zeros = reinterpret_cast<uint8_t*>(b + L.off_zeros);
+  w.order = reinterpret_cast<uint32_t*>(b + L.off_order);
   return w;
 }
 

@@ -47,11 +47,21 @@ struct Ws {
   uint16_t* lists;
   int32_t* counts;
   uint16_t* out;
+  uint8_t* zeros;
+  uint32_t* order;
 };
 
 // Ranking: an 87-bit key per pair, ascending key = (score descending, pair index ascending):
 //   key = ((~bits(score) & 0x7fff'ffff'ffff'ffff) << 24) | pair_index, pair_index < 2^24.
 // The cut of each level is found by an MSD radix select with 8 digits (7 x 11 bits + 10 bits).
+constexpr int kXcds = 8;  // MI355X: 8 accelerator dies, workgroups dispatched round-robin
+
+// Attention work slice of die x holds, for each head, rows [floor(x*Nb/8), floor((x+1)*Nb/8))
+// of that head's similarity order.
+__host__ __device__ inline int xcd_chunk_begin(int x, int Nb) { return (int)(((long long)x * Nb) / kXcds); }
+__host__ __device__ inline int xcd_chunk_size(int x, int Nb) { return xcd_chunk_begin(x + 1, Nb) - xcd_chunk_begin(x, Nb); }
+__host__ __device__ inline int xcd_stride(int bh, int Nb) { return bh * ((Nb + kXcds - 1) / kXcds); }
+
 constexpr int kRankDigits = 8;
 constexpr int kRankBins = 2048;
 enum RankMode : int { kCutNone = 0, kCutAll = 1, kCutKey = 2 };

@@ -401,6 +401,7 @@ hipError_t prepare_d(const Geo& g, const uint16_t* q, const uint16_t* k, const u
   prep_qk_kernel<D><<<dim3(g.Nb, g.bh, 2), kThreads, 0, s>>>(g, q, k, w);
   const size_t na = (size_t)g.bh * D;
   fill_u32_kernel<<<(unsigned)((na + 255) / 256), 256, 0, s>>>(w.v_amax, na, 0u);
+  fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t*>(w.zeros), 64, 0u);
   const int slice = 2048;
   const int slices = (g.N + slice - 1) / slice;
   v_amax_kernel<D><<<dim3(slices, g.bh), kThreads, 0, s>>>(g, v, w.v_amax, slice);
