@@ -107,6 +107,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device copy (a kernel of known "
+                         "read/write size for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the operator is per-head "
@@ -200,6 +203,12 @@ def main():
         "t_roof_over_layer_ms": round(t_roof * 1e3 / ms_per_step, 4),
         "input_gen_s": round(t_gen, 1),
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, Q, K, V)
     print(json.dumps(res), flush=True)

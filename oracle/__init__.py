@@ -19,7 +19,7 @@ Modules, in pipeline order:
   pipeline   one layer end to end, per head
 
 Every function states the passage it follows.  Where the pages leave a step open, the reading used
-is stated in the docstring (readings R1..R29 are listed in the repository design notes).
+is stated in that function's module docstring as a numbered reading (R1..R29).
 
 Parity status: every function is pinned by CPU tests (tests/test_oracle_*.py) against closed forms,
 library routines, exhaustive brute force or invariants.  The end-to-end numbers are "parity unpinned"

@@ -199,9 +199,13 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     asm volatile("" : "+v"(ln));
     const int nl = ln & 31, gl = ln >> 5;
 
-    // ---- S^T = K Q^T
-    f32x16 S[C::MT];
+    // ---- S^T = K Q^T; each finished m-tile's raw maximum is folded in while the next m-tile's
+    // products run (full blocks: the scale is applied to the maximum once, c_scale > 0 keeps the
+    // order and c_scale = 0 gives 0 either way)
     float c_scale = kLog2e * inv_sqrt_d;
+    if (PH == 1) c_scale = s_q * w.k_i8_scale[(size_t)c.bh * g.Nb + kb] * (kLog2e * inv_sqrt_d);
+    f32x16 S[C::MT];
+    float mx = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
       if (PH == 0) {
@@ -211,7 +215,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, lds16(sK + 32 * mt * P::KRB + nl * P::KRB +
                                                16 * swz<P::KRC>(nl, 2 * ks + gl))),
-                                                        __builtin_bit_cast(bf16x8, qop[ks]), acc, 0, 0, 0);
+              __builtin_bit_cast(bf16x8, qop[ks]), acc, 0, 0, 0);
         S[mt] = acc;
       } else if (PH == 1) {
         i32x16 acc = {};
@@ -220,7 +224,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
               __builtin_bit_cast(i32x4, lds16(sK + 32 * mt * P::KRB + nl * P::KRB +
                                               16 * swz<P::KRC>(nl, 2 * ks + gl))),
-                                                      __builtin_bit_cast(i32x4, qop[ks]), acc, 0, 0, 0);
+              __builtin_bit_cast(i32x4, qop[ks]), acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[mt][r] = (float)acc[r];
       } else {
@@ -235,65 +239,31 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         }
         S[mt] = acc;
       }
-      __builtin_amdgcn_sched_barrier(0);  // bound operand lookahead to one m-tile
-    }
-    if (PH == 1) c_scale = s_q * w.k_i8_scale[(size_t)c.bh * g.Nb + kb] * (kLog2e * inv_sqrt_d);
-
-    // ---- online softmax in the log2 domain, one running-max update per key block.
-    // Full blocks: the tile max is taken on the raw scores and scaled once (c_scale > 0 keeps the
-    // order; c_scale = 0 gives 0 either way), and the scale folds into the exponent's FMA.
-    // Edge blocks: scores are scaled and pad keys set to -inf from sBias first.
-    float mx = -INFINITY;
-    if (full) {
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+      if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_scale;
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+      } else {
+        // edge block: scale, then pad keys (and key slots beyond B) get -inf from sBias
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 bias4 = *reinterpret_cast<const float4*>(sBias + 32 * mt + 8 * r4 + 4 * gh);
+          const float4 bias4 = *reinterpret_cast<const float4*>(sBias + 32 * mt + 8 * r4 + 4 * gl);
           S[mt][4 * r4 + 0] = S[mt][4 * r4 + 0] * c_scale + bias4.x;
           S[mt][4 * r4 + 1] = S[mt][4 * r4 + 1] * c_scale + bias4.y;
           S[mt][4 * r4 + 2] = S[mt][4 * r4 + 2] * c_scale + bias4.z;
           S[mt][4 * r4 + 3] = S[mt][4 * r4 + 3] * c_scale + bias4.w;
         }
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      }
     }
+
+    // ---- online softmax statistics in the log2 domain, one running-max update per key block
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (full) mx *= c_scale;
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     const float nbias = PH == 0 ? -m_new : 8.0f - m_new;  // low-bit phases produce 2^8 P
     const float cs = full ? c_scale : 1.0f;
-    // P goes straight into the packed B-operand registers of the P.V products
-    uint32_t pk[C::MT][PH == 0 ? 8 : 4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(S[mt][4 * r4 + e], cs, nbias));
-          psum += p[e];
-        }
-        if (PH == 0) {
-          pk[mt][2 * r4] = pack_bf16(p[0], p[1]);
-          pk[mt][2 * r4 + 1] = pack_bf16(p[2], p[3]);
-        } else {
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          pk[mt][r4] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-        }
-      }
-    if (PH != 0) psum *= 0.00390625f;  // 2^-8, exact
-    l_run = alpha * l_run + psum;
     m_run = m_new;
     if (!__all(alpha == 1.0f)) {
 #pragma unroll
@@ -304,29 +274,36 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
 
     // ---- O^T += V^T P^T.  V goes to LDS first; the next key block's K streams into registers
     // during the products (the load is unconditional -- the last tile re-reads its own block --
-    // so the staging registers are dead between the store at the top and this point; the
-    // scheduling barrier keeps it from being hoisted into the softmax)
+    // so the staging registers are dead between the store at the top and this point).  P is
+    // produced chunk by chunk right before the products that consume it, so its exponentials
+    // can run under the previous chunk's matrix-core work.
     vreg.store(sV, c.tid);
     bar();
-    __builtin_amdgcn_sched_barrier(0);
     kreg.load(k_tile_src<B, D, PH>(g, w, c.bh, kb_next), B, c.tid);
     if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
       kscale = c.tid < B * (D / 32) / 4
                    ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb_next * B) * (D / 32) + 4 * c.tid)
                    : 0x7f7f7f7fu;
+    float psum = 0.0f;
     if (PH == 0) {
 #pragma unroll
       for (int c16 = 0; c16 < B / 16; ++c16) {
-        const int mt = c16 >> 1, wb = 4 * (c16 & 1);
+        const int mt = c16 >> 1, rb = 8 * (c16 & 1);
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(fmaf(S[mt][rb + j], cs, nbias));
+          psum += p[j];
+        }
         const bf16x8 bop = __builtin_bit_cast(
-            bf16x8, make_uint4(pk[mt][wb], pk[mt][wb + 1], pk[mt][wb + 2], pk[mt][wb + 3]));
+            bf16x8, make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                               pack_bf16(p[6], p[7])));
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const bf16x8 a = __builtin_bit_cast(
               bf16x8, lds16(sV + 32 * dt * P::VRB + nl * P::VRB + 16 * swz<P::VRC>(nl, 2 * c16 + gl)));
           O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, O[dt], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
@@ -336,7 +313,20 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         for (int hsel = 0; hsel < 2; ++hsel) {
           const int mt = 2 * c64 + hsel;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) bop[4 * hsel + q4] = mt < C::MT ? (int)pk[mt < C::MT ? mt : 0][q4] : 0;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            int word = 0;
+            if (mt < C::MT) {
+              float p[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(fmaf(S[mt < C::MT ? mt : 0][4 * q4 + e], cs, nbias));
+                psum += p[e];
+              }
+              word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+              word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+            }
+            bop[4 * hsel + q4] = word;
+          }
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
@@ -348,9 +338,10 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
           O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, O[dt], 0, 0, 0, kScaleOne,
                                                                   0, kScaleOne);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      psum *= 0.00390625f;  // 2^-8, exact
     }
+    l_run = alpha * l_run + psum;
   }
 }
 
