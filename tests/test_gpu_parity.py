@@ -251,6 +251,27 @@ def test_deterministic_bitwise():
         assert torch.equal(b.section(ws1, L, name, dt, shape), b.section(ws2, L, name, dt, shape))
 
 
+# ------------------------------------------------------------------------------------ 128-token blocks
+# 128-token blocks (the full-size configurations) at CPU-checkable sizes.
+# 20 x 36 latent with 8 x 16 regions: the last region row holds 4 real rows (keys 64..127 of its
+# blocks are all padding) and the last region column 4 real columns.
+
+@pytest.mark.parametrize("quota", [(0, 0, 0, 10000), (0, 0, 10000, 0), (0, 10000, 0, 0),
+                                   (2000, 2000, 3000, 3000), (7000, 1000, 1000, 1000)])
+@pytest.mark.parametrize("dims", [(128, 8, 16), (64, 8, 16), (128, 4, 32), (128, 16, 8)])
+def test_block128_small(dims, quota):
+    D, rh, rw = dims
+    w = synth.Workload("b128", 2, 20, 36, 2, D, rh, rw, 0.5, quota, seed=4242)
+    _run_case(w)
+
+
+@pytest.mark.parametrize("quota", [(0, 0, 0, 10000), (5000, 1500, 1500, 2000)])
+def test_block128_long_rows(quota):
+    # 80 key blocks per head: long rows that cycle both tile buffers many times
+    w = synth.Workload("b128long", 4, 40, 64, 2, 128, 8, 16, 0.5, quota, seed=4243)
+    _run_case(w)
+
+
 # ------------------------------------------------------------------------------------ full size
 
 @pytest.mark.parametrize("wi", [2, 3, 4])
