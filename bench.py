@@ -1,6 +1,18 @@
 """Benchmark: one attention layer of draft-guided mixed-precision block-sparse attention on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --sweep [--workloads A,B,...] [--out FILE]
+
+The --sweep mode measures every workload (all five by default), one JSON line per case:
+  * the workload's own quota: per-call median and minimum over R timed layers (R = 20, 5 for the
+    91x48x84 few-step shape), ms/layer as the median of the per-layer sum of the four calls,
+    T_roof / T_attention and its real-token variant (N/Np)^2, prepare and restore in GB/s of
+    algorithmic HBM bytes, draft_rank against the draft's fp64 flops, and the shader clock sampled
+    from sysfs during the timed layers;
+  * phase-isolated maps (the same kept-pair count, all at one precision) for 128-token blocks, so
+    each precision's MFMA utilisation is seen alone;
+  * the dense baseline (no skipped pair, all 16-bit) for 128-token blocks, and the speedup of the
+    workload's own quota over it, per attention call and per layer.
 
 A step is one pass of the whole path over one batch of synthetic input, inputs resident in HBM:
 dap_prepare -> dap_draft_rank -> dap_attention -> dap_restore.  Prints one JSON line:
@@ -20,6 +32,7 @@ import json
 import os
 import statistics
 import sys
+import threading
 import time
 
 import numpy as np
@@ -100,6 +113,227 @@ def cpu_baseline(w, Q, K, V, target_s: float = 15.0):
                       f"({t_att:.1f} s); extrapolated linearly to {heads} heads x {Nb} blocks"}
 
 
+# ------------------------------------------------------------------------------------------ sweep
+HBM_PEAK = 8.0e12
+FP64_PEAK = 78.6e12
+
+
+def algorithmic_bytes(L: dict, w):
+    """HBM bytes the method must move, per layer (the layout's sizes, every head):
+    prepare reads Q, K, V and writes the packed bf16 copies, int8 Q/K with per-block scales,
+    MXFP4 Q/K with E8M0 scales, fp8 V^T, the four pooled fp64 descriptors, then reads V once
+    more for the per-channel amax; restore reads the packed output and writes the token-order one;
+    the draft scores are the fp64 [Nb, Nb] map per head."""
+    heads = w.batch * w.heads
+    N, Np, Nb, D = w.N, L["Np"], L["Nb"], w.head_dim
+    prep = heads * (3 * N * D * 2 + 3 * Np * D * 2 + 2 * Np * D + 2 * Nb * 4 +
+                    2 * (Np * D // 2 + Np * D // 32) + Np * D + D * 4 + 4 * Nb * D * 8 +
+                    N * D * 2)
+    restore = heads * (Np * D * 2 + N * D * 2)
+    draft_flops = heads * 4.0 * Nb * Nb * D
+    score_bytes = heads * Nb * Nb * 8
+    return prep, restore, draft_flops, score_bytes
+
+
+class SclkSampler(threading.Thread):
+    """Samples the GPU shader clock from sysfs while a timed region runs (amdgpu exposes the
+    current SCLK as hwmon freq1_input in Hz; pp_dpm_sclk marks the active level with '*').
+    Best effort: reports nothing where neither file is readable."""
+
+    def __init__(self, period_s: float = 0.02):
+        super().__init__(daemon=True)
+        self.period = period_s
+        self.samples = {}
+        self._halt = threading.Event()
+        self.sources = self._find()
+
+    @staticmethod
+    def _find():
+        import glob
+        out = []
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            try:
+                if open(os.path.join(dev, "vendor")).read().strip() != "0x1002":
+                    continue
+            except OSError:
+                continue
+            for f in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "freq1_input"))):
+                out.append((dev, "hwmon", f))
+            p = os.path.join(dev, "pp_dpm_sclk")
+            if os.path.exists(p):
+                out.append((dev, "dpm", p))
+        return out
+
+    def _read(self, kind, path):
+        txt = open(path).read()
+        if kind == "hwmon":
+            return int(txt.strip()) / 1e6
+        for line in txt.splitlines():
+            if line.rstrip().endswith("*"):
+                tok = line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                return float(tok.replace("mhz", ""))
+        return None
+
+    def run(self):
+        if not self.sources:
+            self._run_smi()
+            return
+        while not self._halt.is_set():
+            for dev, kind, path in self.sources:
+                try:
+                    v = self._read(kind, path)
+                except (OSError, ValueError, IndexError):
+                    v = None
+                if v is not None:
+                    self.samples.setdefault((dev, kind), []).append(v)
+            self._halt.wait(self.period)
+
+    def _run_smi(self):
+        """Fallback where sysfs is not readable: poll `rocm-smi --showclocks`."""
+        import re
+        import subprocess
+        pat = re.compile(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", re.I)
+        while not self._halt.is_set():
+            try:
+                txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                                     timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            for m in pat.finditer(txt):
+                self.samples.setdefault(("rocm-smi", "showclocks"), []).append(float(m.group(1)))
+            self._halt.wait(self.period * 10)
+
+    def stop(self):
+        self._halt.set()
+        self.join(timeout=2)
+        # the card under load is the one with the highest median clock
+        best = None
+        for (dev, kind), xs in self.samples.items():
+            med = statistics.median(xs)
+            if best is None or med > best["median_mhz"]:
+                best = {"median_mhz": round(med, 1), "min_mhz": round(min(xs), 1),
+                        "max_mhz": round(max(xs), 1), "samples": len(xs),
+                        "source": f"{os.path.basename(os.path.dirname(dev)) or dev} {kind}"}
+        return best
+
+
+def time_layers(b, cfg, q, k, v, ws, out, warmup: int, reps: int, stream):
+    """HIP events around each of the four calls for `reps` layers after `warmup` untimed ones.
+    Returns per-call lists (ms) and the per-layer sums."""
+    import torch
+    calls = [lambda: b.prepare(cfg, q, k, v, ws), lambda: b.draft_rank(cfg, ws),
+             lambda: b.attention(cfg, ws), lambda: b.restore(cfg, ws, out)]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+    sampler = SclkSampler()
+    sampler.start()
+    for i in range(reps):
+        evs[i][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    sclk = sampler.stop()
+    names = ["prepare", "draft_rank", "attention", "restore"]
+    per = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
+    per["layer"] = [e[0].elapsed_time(e[4]) for e in evs]
+    return per, sclk
+
+
+def measure_case(b, w, quota, q, k, v, dev, warmup, reps, stream, label):
+    import torch
+    cfg = b.Config.from_workload(w, quota_bp=tuple(quota))
+    L = b.workspace_layout(cfg)
+    ws = b.alloc_workspace(cfg, dev)
+    out = torch.empty_like(q)
+    per, sclk = time_layers(b, cfg, q, k, v, ws, out, warmup, reps, stream)
+    del ws, out
+    torch.cuda.empty_cache()
+    heads = w.batch * w.heads
+    flops, t_roof, (n16, n8, n4) = roofline_terms(L, heads, w.head_dim)
+    med = {n: statistics.median(x) for n, x in per.items()}
+    mn = {n: min(x) for n, x in per.items()}
+    prep_b, rest_b, dflops, sbytes = algorithmic_bytes(L, w)
+    real = (w.N / L["Np"]) ** 2
+    t_attn = med["attention"] * 1e-3
+    r = {"case": label, "workload": w.name, "quota_bp_skip_4_8_16": list(quota), "reps": reps,
+         "warmup": warmup, "B": L["B"], "Nb": L["Nb"], "Np": L["Np"], "N": w.N,
+         "kept_pairs_per_head_16_8_4": [n16, n8, n4],
+         "median_ms": {n: round(x, 4) for n, x in med.items()},
+         "min_ms": {n: round(x, 4) for n, x in mn.items()},
+         "ms_per_layer": round(med["layer"], 4),
+         "t_roof_ms": round(t_roof * 1e3, 4),
+         "t_roof_over_t_attn": round(t_roof / t_attn, 4) if t_attn > 0 else None,
+         "t_roof_over_t_attn_real_tokens": round(real * t_roof / t_attn, 4) if t_attn > 0 else None,
+         "real_token_share": round(real, 4),
+         "t_roof_over_layer": round(t_roof * 1e3 / med["layer"], 4),
+         "attn_tflops": round(flops / t_attn / 1e12, 2) if t_attn > 0 else None,
+         "prepare_gbs": round(prep_b / (med["prepare"] * 1e-3) / 1e9, 1),
+         "prepare_frac_hbm": round(prep_b / (med["prepare"] * 1e-3) / HBM_PEAK, 4),
+         "restore_gbs": round(rest_b / (med["restore"] * 1e-3) / 1e9, 1),
+         "restore_frac_hbm": round(rest_b / (med["restore"] * 1e-3) / HBM_PEAK, 4),
+         "draft_rank_fp64_tflops": round(dflops / (med["draft_rank"] * 1e-3) / 1e12, 3),
+         "draft_rank_score_gbs": round(sbytes / (med["draft_rank"] * 1e-3) / 1e9, 1),
+         "algorithmic_bytes": {"prepare": prep_b, "restore": rest_b, "scores": sbytes},
+         "draft_fp64_flops": dflops, "sclk": sclk}
+    if sclk and sclk.get("median_mhz"):
+        r["t_roof_over_t_attn_at_sclk"] = round(t_roof * 2400.0 / sclk["median_mhz"] / t_attn, 4)
+    return r
+
+
+def sweep(args):
+    import torch
+    from video_dit_mixed_amd import binding as b
+    from video_dit_mixed_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    names = args.workloads.split(",") if args.workloads else list(synth.ORDER)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    rows = []
+    sink = open(args.out, "w") if args.out else None
+
+    def emit(r):
+        rows.append(r)
+        line = json.dumps(r)
+        print(line, flush=True)
+        if sink:
+            sink.write(line + "\n")
+            sink.flush()
+
+    for name in names:
+        w = synth.workload(name)
+        reps = args.reps if args.reps else (5 if w.N > 200_000 else 20)
+        print(f"# {name}: generating inputs", flush=True)
+        Q, K, V = synth.make_inputs(w, threads=16)
+        to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = to(Q), to(K), to(V)
+        del Q, K, V
+        base = measure_case(b, w, w.quota_bp, q, k, v, dev, args.warmup, reps, stream, "own")
+        emit(base)
+        kept = 10000 - w.quota_bp[0]
+        if base["B"] == 128 and not args.own_only:
+            for lvl, quota in (("16", (w.quota_bp[0], 0, 0, kept)), ("8", (w.quota_bp[0], 0, kept, 0)),
+                               ("4", (w.quota_bp[0], kept, 0, 0))):
+                emit(measure_case(b, w, quota, q, k, v, dev, args.warmup, reps, stream,
+                                  f"isolated_{lvl}bit"))
+            dense = measure_case(b, w, (0, 0, 0, 10000), q, k, v, dev, args.warmup, reps, stream,
+                                 "dense_16bit")
+            dense["speedup_attention"] = round(dense["median_ms"]["attention"] /
+                                               base["median_ms"]["attention"], 3)
+            dense["speedup_layer"] = round(dense["ms_per_layer"] / base["ms_per_layer"], 3)
+            emit(dense)
+        del q, k, v
+        torch.cuda.empty_cache()
+    if sink:
+        sink.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,12 +344,21 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (a kernel of known "
                          "read/write size for scaling HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="measure every workload: own quota, phase-isolated maps, dense baseline")
+    ap.add_argument("--workloads", default=None, help="comma-separated workloads for --sweep")
+    ap.add_argument("--reps", type=int, default=0, help="timed layers per --sweep case")
+    ap.add_argument("--own-only", action="store_true", help="--sweep: only each workload's quota")
+    ap.add_argument("--out", default=None, help="--sweep: also write the JSON lines here")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the operator is per-head "
               f"and this build measures one GPU's share; multi-GPU head sharding is not built.",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
 
     import torch
     from video_dit_mixed_amd import binding as b

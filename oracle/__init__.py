@@ -17,6 +17,7 @@ Modules, in pipeline order:
   quant      bf16 / e4m3fn / e2m1 rounding, per-block INT8, per-32-channel MXFP4, per-channel FP8 V
   attention  phased online-softmax attention over the 4-level block map
   pipeline   one layer end to end, per head
+  dense      exact dense softmax attention (what the sparse operator approximates)
 
 Every function states the passage it follows.  Where the pages leave a step open, the reading used
 is stated in that function's module docstring as a numbered reading (R1..R29).
@@ -25,5 +26,5 @@ Parity status: every function is pinned by CPU tests (tests/test_oracle_*.py) ag
 library routines, exhaustive brute force or invariants.  The end-to-end numbers are "parity unpinned"
 against the pages: the pages print no worked example.
 """
-from . import layout, quant, draft, attention, pipeline  # noqa: F401
+from . import layout, quant, draft, attention, pipeline, dense  # noqa: F401
 from .pipeline import run, run_head, HeadResult  # noqa: F401

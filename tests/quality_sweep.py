@@ -1,0 +1,196 @@
+"""Output quality of the sparse mixed-precision operator against exact dense attention.
+
+    python tests/quality_sweep.py --leg gpu [--workload hunyuan720p_33x45x80] [--out FILE]
+    python tests/quality_sweep.py --leg cpu [--out FILE]
+
+The pages judge a precision allocation by the relative L2 error of the attention output against
+full attention at a similar latency, and compare single-precision sparse allocations with 4/8-bit
+mixes and the average-only draft with the average/max mix (pchao.org blog on DraftAttention2,
+Figure 1 caption, panel (b); the section 关键结果与论文证据, items on Figure 1(b) and on Table 3 /
+Figure 5).  This script is the synthetic analogue on the seeded inputs: every allocation below is
+either one of the pages' printed quota mixes or one whose precision-weighted MFMA time T_roof
+equals that of the 85/0/7.5/7.5 mix (a 16-bit pair costs 2/2.5 units, an 8-bit pair 1/5 + 1/5,
+a 4-bit pair 1/10.1 + 1/5).
+
+  gpu leg  the HIP path through the C ABI at a full-size layer; the error is taken on a sample of
+           query rows of several heads, against the oracle's exact dense rows (fp64).
+  cpu leg  the oracle alone (phased attention with its emulated roundings) on a reduced layer with
+           the same block geometry, against exact dense attention over every row.
+
+rel-L2 = ||O - O_dense||_2 / ||O_dense||_2 over the rows taken; the bf16 rounding of the output
+alone gives about 1.1e-3.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from oracle import dense as odense  # noqa: E402
+from video_dit_mixed_amd import synth  # noqa: E402
+
+# precision-weighted MFMA time of one kept block pair, in units of (2 B^2 D flops / 1 PFLOP/s)
+COST = {"16": 2 / 2.5, "8": 1 / 5.0 + 1 / 5.0, "4": 1 / 10.1 + 1 / 5.0}
+
+
+def budget(q):
+    """T_roof units (per basis point of pairs) of a quota (skip, 4-bit, 8-bit, 16-bit)."""
+    return q[1] * COST["4"] + q[2] * COST["8"] + q[3] * COST["16"]
+
+
+def equal_budget(ref, share):
+    """A quota with the T_roof of `ref` whose kept pairs split between levels by `share`
+    (fractions of the budget spent on 4-, 8-, 16-bit pairs)."""
+    bud = budget(ref)
+    n4 = int(round(bud * share[0] / COST["4"]))
+    n8 = int(round(bud * share[1] / COST["8"]))
+    n16 = int(round(bud * share[2] / COST["16"]))
+    return (10000 - n4 - n8 - n16, n4, n8, n16)
+
+
+def allocations():
+    ref = (8500, 0, 750, 750)
+    rows = [
+        ("dense 16-bit", (0, 0, 0, 10000), 0.5),
+        ("dense 8-bit", (0, 0, 10000, 0), 0.5),
+        ("dense 4-bit", (0, 10000, 0, 0), 0.5),
+        ("85/0/7.5/7.5 (Table 1 mix)", ref, 0.5),
+        ("85/0/7.5/7.5, avg-pool draft only", ref, 0.0),
+        ("85/0/7.5/7.5, max-pool draft only", ref, 1.0),
+        ("80.7/14.4/4.8/0 (Table 1 4-bit mix)", (8070, 1440, 480, 0), 0.5),
+        ("80.7/14.4/4.8/0, avg-pool draft only", (8070, 1440, 480, 0), 0.0),
+        ("75/15/10/0 (few-step mix)", (7500, 1500, 1000, 0), 0.5),
+        ("equal T_roof: 16-bit only", equal_budget(ref, (0, 0, 1)), 0.5),
+        ("equal T_roof: 8-bit only", equal_budget(ref, (0, 1, 0)), 0.5),
+        ("equal T_roof: 4-bit only", equal_budget(ref, (1, 0, 0)), 0.5),
+        ("equal T_roof: 4/8 mix (half/half)", equal_budget(ref, (0.5, 0.5, 0)), 0.5),
+        ("equal T_roof: 4/8/16 (1/3 each)", equal_budget(ref, (1 / 3, 1 / 3, 1 / 3)), 0.5),
+        ("equal T_roof: 4/8 mix, avg-pool draft only", equal_budget(ref, (0.5, 0.5, 0)), 0.0),
+    ]
+    return rows
+
+
+def rel(out, ref):
+    return float(np.linalg.norm(out - ref) / np.linalg.norm(ref)), float(np.abs(out - ref).max())
+
+
+def gpu_leg(args):
+    import torch
+    from video_dit_mixed_amd import binding as b
+    if not torch.cuda.is_available():
+        sys.exit("the gpu leg needs a GPU")
+    w = synth.workload(args.workload)
+    heads_total = w.batch * w.heads
+    pick = np.linspace(0, heads_total - 1, args.heads).round().astype(int)
+    rng = np.random.default_rng(args.seed)
+    rows = {int(h): np.sort(rng.choice(w.N, args.rows, replace=False)) for h in pick}
+    t0 = time.perf_counter()
+    Q, K, V = synth.make_inputs(w, threads=16)
+    print(f"# {w.name}: inputs {time.perf_counter() - t0:.1f} s", flush=True)
+    t0 = time.perf_counter()
+    ref = {}
+    for h in pick:
+        bb, hh = divmod(int(h), w.heads)
+        ref[int(h)] = odense.dense_attention_rows(Q[bb, hh], K[bb, hh], V[bb, hh], rows[int(h)])
+    print(f"# exact dense rows ({args.heads} heads x {args.rows}): {time.perf_counter() - t0:.1f} s",
+          flush=True)
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(Q), to(K), to(V)
+    del Q, K, V
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    results = []
+    for name, quota, lam in allocations():
+        cfg = b.Config.from_workload(w, quota_bp=tuple(quota), lam=lam)
+        ws = b.alloc_workspace(cfg, dev)
+        b.forward(cfg, q, k, v, ws, out)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.reps)]
+        times = []
+        for i in range(args.reps):
+            ev[2 * i].record(stream)
+            b.attention(cfg, ws)
+            ev[2 * i + 1].record(stream)
+        b.restore(cfg, ws, out)
+        torch.cuda.synchronize()
+        times = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.reps)]
+        flat = out.view(heads_total, w.N, w.head_dim)
+        got, exp = [], []
+        for h in pick:
+            idx = torch.from_numpy(rows[int(h)]).to(dev)
+            got.append(flat[int(h)].index_select(0, idx).float().cpu().numpy().astype(np.float64))
+            exp.append(ref[int(h)])
+        per_head = [rel(g, e)[0] for g, e in zip(got, exp)]
+        r2, mabs = rel(np.concatenate(got), np.concatenate(exp))
+        del ws
+        torch.cuda.empty_cache()
+        r = {"leg": "gpu", "workload": w.name, "allocation": name,
+             "quota_bp_skip_4_8_16": list(quota), "lambda": lam,
+             "t_roof_units_per_bp": round(budget(quota), 2),
+             "attention_ms_median": round(statistics.median(times), 3),
+             "rel_l2": round(r2, 5), "max_abs": round(mabs, 4),
+             "rel_l2_per_head_min_max": [round(min(per_head), 5), round(max(per_head), 5)],
+             "sample": f"{args.rows} random rows in each of heads {pick.tolist()}"}
+        results.append(r)
+        print(json.dumps(r, ensure_ascii=False), flush=True)
+    return results
+
+
+def cpu_leg(args):
+    from oracle import pipeline
+    # same 8x16-region, 128-token block geometry as the full-size layers, smaller latent
+    w = synth.Workload("quality_small_4x24x48", 4, 24, 48, 2, 128, 8, 16, 0.5,
+                       (8500, 0, 750, 750), seed=2024)
+    Q, K, V = synth.make_inputs(w, threads=8)
+    ref = {}
+    for bh in range(w.batch * w.heads):
+        b_, h_ = divmod(bh, w.heads)
+        ref[bh] = odense.dense_attention_rows(Q[b_, h_], K[b_, h_], V[b_, h_])
+    results = []
+    for name, quota, lam in allocations():
+        t0 = time.perf_counter()
+        got, exp = [], []
+        for bh in range(w.batch * w.heads):
+            b_, h_ = divmod(bh, w.heads)
+            r = pipeline.run_head(Q[b_, h_], K[b_, h_], V[b_, h_], T=w.T, H=w.H, W=w.W,
+                                  rh=w.region_h, rw=w.region_w, lam=lam, quota_bp=tuple(quota))
+            got.append(r.out_bf16())
+            exp.append(ref[bh])
+        r2, mabs = rel(np.concatenate(got), np.concatenate(exp))
+        r = {"leg": "cpu-oracle", "workload": w.name, "allocation": name,
+             "quota_bp_skip_4_8_16": list(quota), "lambda": lam,
+             "t_roof_units_per_bp": round(budget(quota), 2), "rel_l2": round(r2, 5),
+             "max_abs": round(mabs, 4), "oracle_s": round(time.perf_counter() - t0, 1)}
+        results.append(r)
+        print(json.dumps(r, ensure_ascii=False), flush=True)
+    return results
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--leg", choices=["gpu", "cpu"], default="gpu")
+    ap.add_argument("--workload", default="hunyuan720p_33x45x80")
+    ap.add_argument("--heads", type=int, default=6)
+    ap.add_argument("--rows", type=int, default=512)
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=77)
+    ap.add_argument("--out", default=None)
+    args = ap.parse_args()
+    res = gpu_leg(args) if args.leg == "gpu" else cpu_leg(args)
+    if args.out:
+        with open(args.out, "w") as f:
+            for r in res:
+                f.write(json.dumps(r, ensure_ascii=False) + "\n")
+
+
+if __name__ == "__main__":
+    main()

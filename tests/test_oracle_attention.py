@@ -198,3 +198,28 @@ def test_prepared_operands_dequantise_to_their_own_tensor():
     amax = np.abs(vreal).max(axis=0)
     big = np.abs(r.vp) >= amax * 2.0 ** -6
     assert np.all(np.abs(deq - r.vp)[big] <= np.abs(r.vp)[big] * 2.0 ** -4 * 1.0001)
+
+
+def test_dense_rows_match_torch_sdpa_and_softmax_identities():
+    """The exact dense reference equals torch's fp64 scaled_dot_product_attention, and for V = I
+    (D = N) its rows are the softmax probabilities: non-negative and summing to 1."""
+    from oracle import dense
+    q, k, v, _ = _small_case(D=32)
+    rows = np.array([0, 5, 17, 100, 125])
+    out = dense.dense_attention_rows(q, k, v, rows, chunk=2)
+    t = lambda a: torch.from_numpy(pipeline.bf16_bits_to_f64(a))[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0].numpy()[rows]
+    assert np.linalg.norm(out - ref) / np.linalg.norm(ref) <= 1e-12
+    # V = identity: the output rows are the attention probabilities themselves
+    N = 40
+    rng = np.random.default_rng(7)
+    qq = synth.f32_to_bf16_bits(rng.standard_normal((N, N)).astype(np.float32))
+    kk = synth.f32_to_bf16_bits(rng.standard_normal((N, N)).astype(np.float32))
+    eye = synth.f32_to_bf16_bits(np.eye(N, dtype=np.float32))
+    P = dense.dense_attention_rows(qq, kk, eye)
+    assert (P >= 0).all() and np.allclose(P.sum(1), 1.0, atol=1e-13)
+    # a key repeated m times gets m times the weight of one copy (softmax over tokens)
+    kk2 = kk.copy()
+    kk2[1] = kk2[0]
+    P2 = dense.dense_attention_rows(qq, kk2, eye)
+    assert np.allclose(P2[:, 0], P2[:, 1], rtol=0, atol=1e-15)
