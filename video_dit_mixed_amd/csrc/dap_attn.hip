@@ -198,6 +198,10 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int nl = ln & 31, gl = ln >> 5;
+    // Logical chunk 2j + gl of operand row nl sits at byte nl*RB + 16*((2j + gl) ^ sw), sw the
+    // row's swizzle; 2j and gl occupy disjoint bits, so that is (nl*RB + 16*(gl ^ sw)) ^ (32 j):
+    // one per-lane base per tile and one XOR per 16-byte read.
+    const int kbase = nl * P::KRB + 16 * (gl ^ ((nl / (16 / P::KRC)) % P::KRC));
 
     // ---- S^T = K Q^T; each finished m-tile's raw maximum is folded in while the next m-tile's
     // products run (full blocks: the scale is applied to the maximum once, c_scale > 0 keeps the
@@ -213,8 +217,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, lds16(sK + 32 * mt * P::KRB + nl * P::KRB +
-                                               16 * swz<P::KRC>(nl, 2 * ks + gl))),
+              __builtin_bit_cast(bf16x8, lds16(sK + 32 * mt * P::KRB + (kbase ^ (32 * ks)))),
               __builtin_bit_cast(bf16x8, qop[ks]), acc, 0, 0, 0);
         S[mt] = acc;
       } else if (PH == 1) {
@@ -222,8 +225,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks)
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-              __builtin_bit_cast(i32x4, lds16(sK + 32 * mt * P::KRB + nl * P::KRB +
-                                              16 * swz<P::KRC>(nl, 2 * ks + gl))),
+              __builtin_bit_cast(i32x4, lds16(sK + 32 * mt * P::KRB + (kbase ^ (32 * ks)))),
               __builtin_bit_cast(i32x4, qop[ks]), acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[mt][r] = (float)acc[r];
@@ -231,7 +233,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) {
-          const uint4 u = lds16(sK + 32 * mt * P::KRB + nl * P::KRB + 16 * swz<P::KRC>(nl, 2 * ks + gl));
+          const uint4 u = lds16(sK + 32 * mt * P::KRB + (kbase ^ (32 * ks)));
           const i32x8 a = {(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
           const i32x8 b = {(int)qop[ks].x, (int)qop[ks].y, (int)qop[ks].z, (int)qop[ks].w, 0, 0, 0, 0};
           const int ksc = (int)sKs[(32 * mt + nl) * (D / 32) + 2 * ks + gl];
@@ -284,6 +286,10 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
       kscale = c.tid < B * (D / 32) / 4
                    ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb_next * B) * (D / 32) + 4 * c.tid)
                    : 0x7f7f7f7fu;
+    // V^T rows: 16-bit tiles read chunks 2 c16 + gl, low-bit tiles chunks 4 c64 + 2 gl + h (h = 0, 1);
+    // the same disjoint-bit argument gives one base per lane and XORs
+    const int vsw = (nl / (16 / P::VRC)) % P::VRC;
+    const int vbase = nl * P::VRB + 16 * (PH == 0 ? (gl ^ vsw) : ((2 * gl) ^ vsw));
     float psum = 0.0f;
     if (PH == 0) {
 #pragma unroll
@@ -300,8 +306,8 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
                                pack_bf16(p[6], p[7])));
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, lds16(sV + 32 * dt * P::VRB + nl * P::VRB + 16 * swz<P::VRC>(nl, 2 * c16 + gl)));
+          const bf16x8 a =
+              __builtin_bit_cast(bf16x8, lds16(sV + 32 * dt * P::VRB + (vbase ^ (32 * c16))));
           O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, O[dt], 0, 0, 0);
         }
       }
@@ -330,9 +336,10 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         }
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const uint8_t* vp = sV + 32 * dt * P::VRB + nl * P::VRB;
-          const uint4 u0 = lds16(vp + 16 * swz<P::VRC>(nl, 4 * c64 + 2 * gl));
-          const uint4 u1 = lds16(vp + 16 * swz<P::VRC>(nl, 4 * c64 + 2 * gl + 1));
+          const uint8_t* vp = sV + 32 * dt * P::VRB;
+          const int va = vbase ^ (64 * c64);
+          const uint4 u0 = lds16(vp + va);
+          const uint4 u1 = lds16(vp + (va ^ 16));
           const i32x8 a = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
                            (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
           O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, O[dt], 0, 0, 0, kScaleOne,

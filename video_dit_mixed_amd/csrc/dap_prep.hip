@@ -308,21 +308,31 @@ __device__ __forceinline__ int vt8_pos(int m) {
   return (m & ~63) | (((k >> 2) & 1) << 5) | (((k >> 5) & 1) << 4) | (((k >> 3) & 3) << 2) |
          (k & 3);
 }
+// Key held at position p of the FP8 V^T row (the inverse of vt8_pos): position 32g + 16a + 4b + e
+// of a 64-key chunk holds key 32a + 8b + 4g + e.
+__device__ __forceinline__ int vt8_key(int p) {
+  const int k = p & 63;
+  return (p & ~63) | (((k >> 4) & 1) << 5) | (((k >> 2) & 3) << 3) | (((k >> 5) & 1) << 2) |
+         (k & 3);
+}
 
 // ------------------------------------------------------------------------------------ V pack
+// One workgroup per (block, head).  The block's B token rows are gathered into LDS in their
+// natural [key][channel] order (rows padded by 4 bytes so that reads of one channel across keys
+// spread over the banks); then every thread emits whole 16-byte chunks of the transposed outputs,
+// reading the chunk's keys for its channel from LDS: consecutive threads cover consecutive chunks
+// of one output row, so the global stores are contiguous.  FP8 codes come from the hardware
+// converter (round to nearest even; |x * r| <= 448 by construction of r, so no saturation case).
 template <int D>
 __global__ __launch_bounds__(kThreads) void v_pack_kernel(Geo g, const uint16_t* __restrict__ v,
                                                          Ws w) {
-  constexpr int CH = D / 8;
-  constexpr int RP = kThreads / CH;
-  constexpr int MAXP = 128 / RP;
-  constexpr int KPMAX = 128;                      // largest B and kp8
-  __shared__ uint16_t s_vt16[D][KPMAX + 8];       // +8 elements: stagger LDS rows
-  __shared__ uint8_t s_vt8[D][KPMAX + 16];
+  constexpr int CH = D / 8;                 // 16-byte chunks per token row
+  constexpr int PITCH = 2 * D + 4;          // LDS bytes per key row
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[128 * PITCH];
   __shared__ float s_r[D];
 
   const int b = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, c = tid % CH, r0 = tid / CH;
+  const int tid = threadIdx.x;
   const int B = g.B, kp8 = g.kp8;
   const BlockCoord bc = block_coord(g, b);
   const uint16_t* src = v + (size_t)bh * g.N * D;
@@ -332,59 +342,61 @@ __global__ __launch_bounds__(kThreads) void v_pack_kernel(Geo g, const uint16_t*
     s_r[tid] = a > 0.0f ? 448.0f / a : 0.0f;
     if (b == 0) w.v_scale[(size_t)bh * D + tid] = a > 0.0f ? a / 448.0f : 0.0f;
   }
-  // zero the unused FP8 positions (keys >= B when B < 64)
-  for (int i = tid; i < D * kp8; i += kThreads) {
-    const int d = i / kp8, pos = i - (i / kp8) * kp8;
-    s_vt8[d][pos] = 0;
-  }
-  __syncthreads();
-
-#pragma unroll
-  for (int p = 0; p < MAXP; ++p) {
-    const int r = r0 + p * RP;
-    if (r >= B) continue;
-    uint4 raw = make_uint4(0, 0, 0, 0);
+  // gather: key r of the block is region pixel (iy, ix) = (r / rw, r % rw); pad keys are 0
+  for (int i = tid; i < B * CH; i += kThreads) {
+    const int r = i / CH, c = i - (i / CH) * CH;
     const int iy = r / g.rw, ix = r - (r / g.rw) * g.rw;
+    uint4 raw = make_uint4(0, 0, 0, 0);
     if (iy < bc.vh && ix < bc.vw) {
       const size_t n = ((size_t)bc.t * g.H + bc.ry * g.rh + iy) * g.W + bc.rx * g.rw + ix;
       raw = *reinterpret_cast<const uint4*>(src + n * D + c * 8);
     }
-    const int p16 = vt16_pos(r), p8 = vt8_pos(r);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t h = (word_of(raw, j >> 1) >> ((j & 1) ? 16 : 0)) & 0xffffu;
-      const int d = c * 8 + j;
-      s_vt16[d][p16] = (uint16_t)h;
-      s_vt8[d][p8] = (uint8_t)e4m3_code(bf16_to_f32(h) * s_r[d]);
-    }
+    uint32_t* dstw = reinterpret_cast<uint32_t*>(s_v + r * PITCH + 16 * c);
+    dstw[0] = raw.x;
+    dstw[1] = raw.y;
+    dstw[2] = raw.z;
+    dstw[3] = raw.w;
   }
   __syncthreads();
+  auto val = [&](int key, int d) -> uint32_t {
+    return *reinterpret_cast<const uint16_t*>(s_v + key * PITCH + 2 * d);
+  };
 
-  // write rows d: bf16 row of B elements, fp8 row of kp8 bytes (8-byte lanes)
+  // bf16 V^T rows: output position p of row d holds key vt16_pos^-1(p) (an involution)
   if (g.need16) {
     uint16_t* dst = w.vt_bf16 + ((size_t)bh * g.Nb + b) * (size_t)D * B;
-    const int per_row = B / 4;  // 8-byte chunks
-    for (int i = tid; i < D * per_row; i += kThreads) {
-      const int d = i / per_row, ch = i - (i / per_row) * per_row;
-      const uint16_t* s = &s_vt16[d][ch * 4];
-      uint2 val = make_uint2((uint32_t)s[0] | ((uint32_t)s[1] << 16),
-                             (uint32_t)s[2] | ((uint32_t)s[3] << 16));
-      *reinterpret_cast<uint2*>(dst + (size_t)d * B + ch * 4) = val;
+    const int cpr = B / 8;  // 16-byte chunks per output row
+    for (int q = tid; q < D * cpr; q += kThreads) {
+      const int d = q / cpr, cc = q - (q / cpr) * cpr;
+      uint32_t wv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wv[j] = val(vt16_pos(8 * cc + 2 * j), d) | (val(vt16_pos(8 * cc + 2 * j + 1), d) << 16);
+      *reinterpret_cast<uint4*>(dst + (size_t)d * B + 8 * cc) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
   }
+  // e4m3 V^T rows of kp8 bytes: position p holds key vt8_key(p); keys >= B are 0
   if (g.need8 || g.need4) {
     uint8_t* dst = w.vt_fp8 + ((size_t)bh * g.Nb + b) * (size_t)D * kp8;
-    const int per_row = kp8 / 8;
-    for (int i = tid; i < D * per_row; i += kThreads) {
-      const int d = i / per_row, ch = i - (i / per_row) * per_row;
-      const uint8_t* s = &s_vt8[d][ch * 8];
-      uint32_t lo = 0, hi = 0;
+    const int cpr = kp8 / 16;
+    for (int q = tid; q < D * cpr; q += kThreads) {
+      const int d = q / cpr, cc = q - (q / cpr) * cpr;
+      const float r = s_r[d];
+      uint32_t wv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lo |= (uint32_t)s[j] << (8 * j);
-        hi |= (uint32_t)s[4 + j] << (8 * j);
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = vt8_key(16 * cc + 4 * j + e);
+          x[e] = key < B ? bf16_to_f32(val(key, d)) * r : 0.0f;
+        }
+        int word = (int)__float_as_uint(x[0]);  // any value: both halves are written below
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], word, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
+        wv[j] = (uint32_t)word;
       }
-      *reinterpret_cast<uint2*>(dst + (size_t)d * kp8 + ch * 8) = make_uint2(lo, hi);
+      *reinterpret_cast<uint4*>(dst + (size_t)d * kp8 + 16 * cc) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
   }
 }
