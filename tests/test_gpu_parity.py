@@ -136,9 +136,9 @@ def _sample_blocks(r, S, k=12, seed=0):
     return sorted(pick)
 
 
-def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None):
+def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None, inputs=None):
     log(f"case {w.name} quota={w.quota_bp} lam={w.lam} batch={w.batch}")
-    Q, K, V = _inputs(w, exact_heads)
+    Q, K, V = _inputs(w, exact_heads) if inputs is None else inputs
     cfg = b.Config.from_workload(w)
     q, k, v = to_device(Q, K, V)
     log("gpu run")
@@ -270,6 +270,17 @@ def test_block128_long_rows(quota):
     # 80 key blocks per head: long rows that cycle both tile buffers many times
     w = synth.Workload("b128long", 4, 40, 64, 2, 128, 8, 16, 0.5, quota, seed=4243)
     _run_case(w)
+
+
+@pytest.mark.parametrize("quota", [(5000, 1500, 1500, 2000), (8500, 0, 750, 750)])
+def test_all_draft_scores_tied(quota):
+    # Head 0 has Q = 0, so every pooled logit is 0 and every draft score is exactly 1/Nb: the
+    # ranking falls back to the pair index and every pair shares every cut's key prefix (the rank
+    # candidate list overflows and that head keeps scanning all pairs).  Head 1 is ordinary.
+    w = synth.Workload("ties", 4, 40, 64, 2, 128, 8, 16, 0.5, quota, seed=4244)
+    Q, K, V = synth.make_inputs(w)
+    Q[0, 0] = 0
+    _run_case(w, inputs=(Q, K, V))
 
 
 # ------------------------------------------------------------------------------------ full size

@@ -6,7 +6,7 @@
 // Figure 2 caption.  fp64 keeps the scores exact enough that the per-head ranking (and so the block
 // map) is reproducible bit for bit.
 //
-// Kernels: draft_logits -- a 64x64-tile fp64 GEMM per (head, map), writing L_avg into the score
+// Kernels: draft_logits -- a 128x128-tile fp64 GEMM per (head, map), writing L_avg into the score
 // buffer and L_max into a scratch buffer; draft_mix -- one workgroup per query region row,
 // exponentials staged in LDS, writes A over L_avg.
 #pragma clang fp contract(off)
@@ -16,29 +16,33 @@
 namespace dap {
 namespace {
 
-constexpr int kTile = 64;
-constexpr int kKc = 16;
+constexpr int kTile = 128;  // output tile edge (rows and columns of one workgroup)
+constexpr int kKc = 16;     // channels staged per step
 
+// 256 threads, each an 8 x 8 block of outputs (rows 8 ty + i; columns 2 tx + 32 jj + e, jj < 4,
+// e < 2): per channel a thread reads its 8 Q values and 8 K values as four 16-byte LDS loads each
+// (the K loads of 16 neighbouring threads are contiguous, so bank-conflict free) and does 64 fused
+// multiply-adds.  Each output is one fma chain over the channels in ascending order.
 template <int D>
 __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, Ws w) {
-  __shared__ double sQ[kKc][kTile + 1];
-  __shared__ double sK[kKc][kTile + 1];
+  __shared__ __attribute__((aligned(16))) double sQ[kKc][kTile + 2];
+  __shared__ __attribute__((aligned(16))) double sK[kKc][kTile + 2];
   const int bh = blockIdx.z >> 1, which = blockIdx.z & 1;
   const double* qbar = (which == 0 ? w.q_avg : w.q_max) + (size_t)bh * g.Nb * D;
   const double* kbar = (which == 0 ? w.k_avg : w.k_max) + (size_t)bh * g.Nb * D;
   double* dst = (which == 0 ? w.scores : w.lmax) + (size_t)bh * g.pairs;
   const int row0 = blockIdx.y * kTile, col0 = blockIdx.x * kTile;
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  double acc[4][4];
+  double acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
 
   for (int d0 = 0; d0 < D; d0 += kKc) {
-    // 64 rows x 16 channels of each operand: 1024 values, 4 per thread
+    // 128 rows x 16 channels of each operand: 2048 values, 8 per thread
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int e = tid + i * 256;
       const int r = e / kKc, c = e % kKc;
       const int qr = row0 + r, kr = col0 + r;
@@ -46,30 +50,35 @@ __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, Ws w) {
       sK[c][r] = kr < g.Nb ? kbar[(size_t)kr * D + d0 + c] : 0.0;
     }
     __syncthreads();
-#pragma unroll
+#pragma unroll 2
     for (int c = 0; c < kKc; ++c) {
-      double a[4], b[4];
+      double a[8], b[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = sQ[c][ty + 16 * i];
-        b[i] = sK[c][tx + 16 * i];
+      for (int i = 0; i < 8; i += 2) {
+        const double2 qa = *reinterpret_cast<const double2*>(&sQ[c][8 * ty + i]);
+        const double2 kb = *reinterpret_cast<const double2*>(&sK[c][2 * tx + 16 * i]);
+        a[i] = qa.x;
+        a[i + 1] = qa.y;
+        b[i] = kb.x;
+        b[i + 1] = kb.y;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
     }
     __syncthreads();
   }
-  const double sq = sqrt((double)D);
+  const double inv_sq = 1.0 / sqrt((double)D);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = row0 + ty + 16 * i;
+  for (int i = 0; i < 8; ++i) {
+    const int r = row0 + 8 * ty + i;
     if (r >= g.Nb) continue;
+    double* drow = dst + (size_t)r * g.Nb;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = col0 + tx + 16 * j;
-      if (c < g.Nb) dst[(size_t)r * g.Nb + c] = acc[i][j] / sq;
+    for (int j = 0; j < 8; ++j) {
+      const int col = col0 + 2 * tx + 16 * (j & ~1) + (j & 1);  // b[j] of column 2 tx + 32 (j/2) + j%2
+      if (col < g.Nb) drow[col] = acc[i][j] * inv_sq;
     }
   }
 }
@@ -119,7 +128,8 @@ __global__ __launch_bounds__(256) void draft_mix_kernel(Geo g, Ws w) {
   sa = block_reduce(sa, false, s_red);
   sm = block_reduce(sm, false, s_red);
   const double lam = g.lambda, oml = 1.0 - g.lambda;
-  for (int j = threadIdx.x; j < Nb; j += blockDim.x) La[j] = oml * (ea[j] / sa) + lam * (em[j] / sm);
+  const double ra = 1.0 / sa, rm = 1.0 / sm;
+  for (int j = threadIdx.x; j < Nb; j += blockDim.x) La[j] = oml * (ea[j] * ra) + lam * (em[j] * rm);
 }
 
 template <int D>

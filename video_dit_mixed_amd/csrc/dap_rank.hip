@@ -12,6 +12,10 @@
 // key exactly in 8 digit passes (7 x 11 bits + 10 bits); each pass is a histogram over all pairs
 // whose key shares the cut's known prefix (LDS histograms, flushed with integer atomics, so the
 // result does not depend on scheduling), then a one-workgroup scan per head picks the digit.
+// After the first two digits (exponent and 11 mantissa bits) the pairs that still share a cut's
+// prefix are few: they are compacted once into a candidate list (in the max-pool logits map, which
+// is dead after the draft mix) and the remaining six passes histogram only that list.  A head whose
+// candidates overflow the list keeps scanning all its pairs.
 // Finally one wave per query row classifies its pairs against the cut keys, writes the uint8 map
 // and the per-level key-block lists (ascending kb) with ballot/popcount compaction.
 #include "dap_internal.h"
@@ -50,8 +54,19 @@ __global__ void rank_init_kernel(Geo g, RankCut* st, uint32_t* hist) {
 constexpr int kHistThreads = 256;
 constexpr int kPerThread = 64;
 constexpr int kChunk = kHistThreads * kPerThread;
+constexpr int kCompactPass = 1;  // candidates are compacted after this pass's digit is chosen
 
-__global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(Geo g, const double* __restrict__ scores,
+// Candidate list of one head inside its region of the max-pool logits map (pairs x 8 bytes):
+// cap = pairs / 2 score bit patterns (8 bytes each) followed by cap pair indices (4 bytes each).
+__device__ __forceinline__ long long cand_cap(const Geo& g) { return g.pairs / 2; }
+__device__ __forceinline__ unsigned long long* cand_bits(const Geo& g, const Ws& w, int bh) {
+  return reinterpret_cast<unsigned long long*>(w.lmax + (size_t)bh * g.pairs);
+}
+__device__ __forceinline__ uint32_t* cand_idx(const Geo& g, const Ws& w, int bh) {
+  return reinterpret_cast<uint32_t*>(cand_bits(g, w, bh) + cand_cap(g));
+}
+
+__global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(Geo g, Ws w, const double* __restrict__ scores,
                                                                  const RankCut* __restrict__ st,
                                                                  uint32_t* __restrict__ hist, int pass) {
   __shared__ uint32_t s_h[3][kRankBins];
@@ -67,16 +82,24 @@ __global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(Geo g, const do
     any |= active[j];
   }
   if (!any) return;
+  // candidate mode: after the compaction, unless this head's list overflowed
+  const long long ncand = pass > kCompactPass ? (long long)st[bh * 3].pad : -1;
+  const bool cand = ncand >= 0 && ncand <= cand_cap(g);
+  const unsigned long long* cb = cand_bits(g, w, bh);
+  const uint32_t* ci = cand_idx(g, w, bh);
+  const long long n = cand ? ncand : (long long)g.pairs;
+  const long long i0 = (long long)blockIdx.x * kChunk;
+  if (i0 >= n) return;  // uniform per workgroup
+  const long long i1 = min(n, i0 + kChunk);
   for (int i = threadIdx.x; i < 3 * kRankBins; i += kHistThreads) (&s_h[0][0])[i] = 0;
   __syncthreads();
   const int shift = rank_digit_shift(pass);
   const int top = shift + rank_digit_width(pass);
   const uint32_t mask = (1u << rank_digit_width(pass)) - 1u;
   const double* sc = scores + (size_t)bh * g.pairs;
-  const long long i0 = (long long)blockIdx.x * kChunk;
-  const long long i1 = min((long long)g.pairs, i0 + kChunk);
   for (long long i = i0 + threadIdx.x; i < i1; i += kHistThreads) {
-    const u128 key = pair_key(sc[i], (uint32_t)i);
+    const u128 key = cand ? pair_key(__longlong_as_double((long long)cb[i]), ci[i])
+                          : pair_key(sc[i], (uint32_t)i);
     const u128 hi = key >> top;
     const uint32_t digit = (uint32_t)(key >> shift) & mask;
 #pragma unroll
@@ -88,6 +111,61 @@ __global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(Geo g, const do
   for (int i = threadIdx.x; i < 3 * kRankBins; i += kHistThreads) {
     const uint32_t v = (&s_h[0][0])[i];
     if (v) atomicAdd(&gh[i], v);
+  }
+}
+
+// Appends every pair whose key shares an active cut's prefix (known after pass kCompactPass) to
+// the head's candidate list.  Slots come from one atomic per wave, so the list order depends on
+// scheduling; the histograms that read it do not.  The count keeps growing past the capacity, which
+// tells later passes that the list overflowed.
+__global__ __launch_bounds__(kHistThreads) void rank_compact_kernel(Geo g, Ws w, const double* __restrict__ scores,
+                                                                    RankCut* __restrict__ st) {
+  const int bh = blockIdx.y;
+  bool active[3];
+  u128 prefix[3];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const RankCut c = st[bh * 3 + j];
+    active[j] = c.mode == kCutKey;
+    prefix[j] = make_u128(c.prefix_hi, c.prefix_lo);
+    any |= active[j];
+  }
+  if (!any) return;
+  const int top = rank_digit_shift(kCompactPass);  // bits below the known prefix
+  const double* sc = scores + (size_t)bh * g.pairs;
+  unsigned long long* cb = cand_bits(g, w, bh);
+  uint32_t* ci = cand_idx(g, w, bh);
+  const long long cap = cand_cap(g);
+  int* counter = &st[bh * 3].pad;
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const long long i0 = (long long)blockIdx.x * kChunk;
+  const long long i1 = min((long long)g.pairs, i0 + kChunk);
+  for (long long b0 = i0; b0 < i1; b0 += kHistThreads) {  // same trip count for every lane
+    const long long i = b0 + threadIdx.x;
+    bool hit = false;
+    unsigned long long bits = 0;
+    if (i < i1) {
+      const double v = sc[i];
+      bits = (unsigned long long)__double_as_longlong(v);
+      const u128 hi = pair_key(v, (uint32_t)i) >> top;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) hit |= active[j] && hi == prefix[j];
+    }
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      int wbase = 0;
+      if (lane == 0) wbase = atomicAdd(counter, __popcll(m));
+      wbase = __shfl(wbase, 0);
+      if (hit) {
+        const long long slot = (long long)wbase + __popcll(m & below);
+        if (slot < cap) {
+          cb[slot] = bits;
+          ci[slot] = (uint32_t)i;
+        }
+      }
+    }
   }
 }
 
@@ -283,8 +361,10 @@ hipError_t launch_rank(const Geo& g, const Ws& w, hipStream_t s) {
   rank_init_kernel<<<g.bh, 256, 0, s>>>(g, st, w.rank_hist);
   const unsigned chunks = (unsigned)((g.pairs + kChunk - 1) / kChunk);
   for (int pass = 0; pass < kRankDigits; ++pass) {
-    rank_hist_kernel<<<dim3(chunks, g.bh), kHistThreads, 0, s>>>(g, w.scores, st, w.rank_hist, pass);
+    rank_hist_kernel<<<dim3(chunks, g.bh), kHistThreads, 0, s>>>(g, w, w.scores, st, w.rank_hist, pass);
     rank_select_kernel<<<g.bh, 256, 0, s>>>(st, w.rank_hist, pass);
+    if (pass == kCompactPass)
+      rank_compact_kernel<<<dim3(chunks, g.bh), kHistThreads, 0, s>>>(g, w, w.scores, st);
   }
   rank_assign_kernel<<<dim3((g.Nb + 3) / 4, g.bh), 256, 0, s>>>(g, w.scores, st, w.map, w.lists,
                                                                    w.counts);
