@@ -85,8 +85,24 @@ struct RowCtx {
   int bh, qb, tid, n, gh;
   bool qok;
   size_t qrow;            // packed row of this lane's query
-  const uint16_t* list;   // key-block list of the row
+  const uint32_t* lists;  // all key-block lists, as 32-bit words
+  size_t lbase;           // index of this row's first list entry
 };
+
+// Entry i of the row's key-block list.  The list holds 16-bit entries; the 32-bit word holding
+// entry i is read at a wave-uniform address, so it is a scalar load (a 16-bit vector load would be
+// waited for with vmcnt, which also waits for every tile load in flight).
+typedef __attribute__((address_space(4))) const uint32_t* const_u32_ptr;  // read-only in this kernel
+
+__device__ __forceinline__ uint32_t uniform_load(const uint32_t* p) {
+  return *reinterpret_cast<const_u32_ptr>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ int list_at(const RowCtx& c, int i) {
+  const size_t e = c.lbase + (size_t)i;
+  const uint32_t wv = uniform_load(c.lists + (e >> 1));
+  return (int)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+}
 
 // One key block's operand tile held in registers between its global load and its LDS store.
 // Slot s (16 bytes) of a tile of rows with RC chunks sits at LDS byte 16*s and holds row s / RC,
@@ -157,7 +173,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     qop[ks] = c.qok ? *reinterpret_cast<const uint4*>(base) : make_uint4(0, 0, 0, 0);
     qsc[ks] = (PH == 2 && c.qok) ? (int)w.q_e8m0[c.qrow * (D / 32) + 2 * ks + gh] : 127;
   }
-  if (PH == 1) s_q = w.q_i8_scale[(size_t)c.bh * g.Nb + c.qb];
+  if (PH == 1) s_q = __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(w.q_i8_scale) + (size_t)c.bh * g.Nb + c.qb));
   using P = PhaseCfg<B, D, PH>;
   const int lane = c.tid & 63;
   TileRegs<C::KT, P::KRC, C::NT> kreg;
@@ -166,7 +182,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
 
   // prologue: the first key block's tiles go to registers
   {
-    const int kb0 = __builtin_amdgcn_readfirstlane(c.list[off]);
+    const int kb0 = list_at(c, off);
     kreg.load(k_tile_src<B, D, PH>(g, w, c.bh, kb0), B, c.tid);
     if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
       kscale = c.tid < B * (D / 32) / 4
@@ -175,8 +191,8 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
   }
 
   for (int it = 0; it < np; ++it) {
-    const int kb = __builtin_amdgcn_readfirstlane(c.list[off + it]);
-    const int kb_next = it + 1 < np ? __builtin_amdgcn_readfirstlane(c.list[off + it + 1]) : kb;
+    const int kb = list_at(c, off + it);
+    const int kb_next = it + 1 < np ? list_at(c, off + it + 1) : kb;
     // real extent of key block kb (regions at the high-y / high-x edge hold padding)
     const int per = g.nby * g.nbx;
     const int rem = kb % per;
@@ -207,7 +223,9 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     // products run (full blocks: the scale is applied to the maximum once, c_scale > 0 keeps the
     // order and c_scale = 0 gives 0 either way)
     float c_scale = kLog2e * inv_sqrt_d;
-    if (PH == 1) c_scale = s_q * w.k_i8_scale[(size_t)c.bh * g.Nb + kb] * (kLog2e * inv_sqrt_d);
+    if (PH == 1)
+      c_scale = s_q * __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(w.k_i8_scale) + (size_t)c.bh * g.Nb + kb)) *
+                (kLog2e * inv_sqrt_d);
     f32x16 S[C::MT];
     float mx = -INFINITY;
 #pragma unroll
@@ -369,8 +387,8 @@ void attn_kernel(Geo g, Ws w) {
     const int x = blockIdx.x & (kXcds - 1), j = blockIdx.x / kXcds;
     if (j >= g.bh * xcd_chunk_size(x, Nb)) return;
     const uint32_t item = w.order[(size_t)x * xcd_stride(g.bh, Nb) + j];
-    c.bh = (int)(item >> 16);
-    c.qb = (int)(item & 0xffff);
+    c.bh = __builtin_amdgcn_readfirstlane((int)(item >> 16));
+    c.qb = __builtin_amdgcn_readfirstlane((int)(item & 0xffff));
   }
   c.tid = threadIdx.x;
   const int wv = c.tid >> 6, lane = c.tid & 63;
@@ -379,12 +397,13 @@ void attn_kernel(Geo g, Ws w) {
   const int qr = 32 * wv + c.n;  // query row inside the block
   c.qok = qr < B;
   c.qrow = (size_t)c.bh * g.Np + (size_t)c.qb * B + qr;
-  c.list = w.lists + (size_t)c.bh * g.pairs + (size_t)c.qb * Nb;
+  c.lists = reinterpret_cast<const uint32_t*>(w.lists);
+  c.lbase = (size_t)c.bh * g.pairs + (size_t)c.qb * Nb;
 
   const int32_t* cnt = w.counts + ((size_t)c.bh * Nb + c.qb) * 4;
-  const int n16 = __builtin_amdgcn_readfirstlane(cnt[0]);
-  const int n8 = __builtin_amdgcn_readfirstlane(cnt[1]);
-  const int n4 = __builtin_amdgcn_readfirstlane(cnt[2]);
+  const int n16 = (int)uniform_load(reinterpret_cast<const uint32_t*>(cnt));
+  const int n8 = (int)uniform_load(reinterpret_cast<const uint32_t*>(cnt) + 1);
+  const int n4 = (int)uniform_load(reinterpret_cast<const uint32_t*>(cnt) + 2);
 
   f32x16 O[C::DT];
 #pragma unroll
