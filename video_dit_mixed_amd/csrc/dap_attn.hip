@@ -34,7 +34,11 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(16))) int i32x16;
 
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource: 32-bit data format, no swizzle, no index.
+constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kScaleOne = 0x7f7f7f7f;  // E8M0 127 = 2^0 in every byte
 
 template <int B, int D>
@@ -113,13 +117,18 @@ struct TileRegs {
   static_assert(ROWS * RC % NT == 0, "tile must split evenly over the threads");
   uint4 v[N];
 
+  // Buffer loads: a wave-uniform resource for the tile plus a 32-bit offset per lane (a 64-bit
+  // address per lane costs more to issue), and rows >= valid fall outside the resource's range,
+  // which reads as zero.
   __device__ __forceinline__ void load(const uint8_t* __restrict__ gsrc, int valid, int tid) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(gsrc), (short)0, valid * RC * 16, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int sl = tid + j * NT;
       const int r = sl / RC, pc = sl - (sl / RC) * RC;
-      v[j] = r < valid ? *reinterpret_cast<const uint4*>(gsrc + (size_t)r * (RC * 16) + 16 * swz<RC>(r, pc))
-                       : make_uint4(0, 0, 0, 0);
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, r * (RC * 16) + 16 * swz<RC>(r, pc), 0, 0);
+      v[j] = make_uint4(t[0], t[1], t[2], t[3]);
     }
   }
   __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
