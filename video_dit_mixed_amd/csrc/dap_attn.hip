@@ -423,15 +423,26 @@ void attn_kernel(Geo g, Ws w) {
 
   if (n16 > 0) run_phase<B, D, 0>(g, w, c, O, m_run, l_run, n16, 0, sK, sV, sKs, sBias);
   const bool lowbit = n8 + n4 > 0;
-  if (lowbit) {
-    // accumulator unit change at the 16 -> low-bit boundary: channel d x 2^8 / s_V[d]
+  // The FP8 V scales of this lane's accumulator channels 32 dt + 8 r4 + 4 gh + e: four
+  // consecutive channels per (dt, r4), fetched together as 16-byte loads.
+  auto v_scales = [&](float4 (&sv)[C::DT][4]) {
+    const float* vs = w.v_scale + (size_t)c.bh * D + 4 * c.gh;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * dt + 8 * (r >> 2) + 4 * c.gh + (r & 3);
-        const float sv = w.v_scale[(size_t)c.bh * D + d];
-        O[dt][r] *= sv > 0.0f ? 256.0f / sv : 0.0f;
+      for (int r4 = 0; r4 < 4; ++r4) sv[dt][r4] = *reinterpret_cast<const float4*>(vs + 32 * dt + 8 * r4);
+  };
+  if (lowbit) {
+    // accumulator unit change at the 16 -> low-bit boundary: channel d x 2^8 / s_V[d]
+    float4 sv[C::DT][4];
+    v_scales(sv);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float s4[4] = {sv[dt][r4].x, sv[dt][r4].y, sv[dt][r4].z, sv[dt][r4].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[dt][4 * r4 + e] *= s4[e] > 0.0f ? 256.0f / s4[e] : 0.0f;
       }
   }
   if (n8 > 0) run_phase<B, D, 1>(g, w, c, O, m_run, l_run, n8, n16, sK, sV, sKs, sBias);
@@ -442,16 +453,19 @@ void attn_kernel(Geo g, Ws w) {
   const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
   if (c.qok) {
     uint16_t* dst = w.out + c.qrow * D;
+    float4 sv[C::DT][4];
+    if (lowbit) v_scales(sv);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * dt + 8 * r4 + 4 * c.gh;
+        const float s4[4] = {sv[dt][r4].x, sv[dt][r4].y, sv[dt][r4].z, sv[dt][r4].w};
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float o = O[dt][4 * r4 + e];
-          if (lowbit) o *= w.v_scale[(size_t)c.bh * D + d0 + e] * 0.00390625f;
+          if (lowbit) o *= s4[e] * 0.00390625f;
           v[e] = o * inv_l;
         }
         const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1], b2 = (__bf16)v[2], b3 = (__bf16)v[3];
