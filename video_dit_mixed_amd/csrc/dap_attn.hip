@@ -235,10 +235,9 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     if (PH == 1)
       c_scale = s_q * __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(w.k_i8_scale) + (size_t)c.bh * g.Nb + kb)) *
                 (kLog2e * inv_sqrt_d);
-    f32x16 S[C::MT];
+    f32x16 S[C::MT];  // the 8-bit phase keeps its int32 sums here (bit patterns) until converted
     float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
+    auto qk_tile = [&](int mt) {
       if (PH == 0) {
         f32x16 acc = {};
 #pragma unroll
@@ -254,8 +253,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(
               __builtin_bit_cast(i32x4, lds16(sK + 32 * mt * P::KRB + (kbase ^ (32 * ks)))),
               __builtin_bit_cast(i32x4, qop[ks]), acc, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[mt][r] = (float)acc[r];
+        S[mt] = __builtin_bit_cast(f32x16, acc);
       } else {
         f32x16 acc = {};
 #pragma unroll
@@ -267,6 +265,13 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
           acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, 0, ksc, 0, qsc[ks]);
         }
         S[mt] = acc;
+      }
+    };
+    auto qk_post = [&](int mt) {
+      if (PH == 1) {
+        const i32x16 si = __builtin_bit_cast(i32x16, S[mt]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[mt][r] = (float)si[r];
       }
       if (full) {
 #pragma unroll
@@ -284,7 +289,16 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
       }
+    };
+    // one m-tile of lookahead: the products of m-tile mt are issued before m-tile mt - 1's
+    // conversion and maximum, which then run while the matrix core works
+    qk_tile(0);
+#pragma unroll
+    for (int mt = 1; mt < C::MT; ++mt) {
+      qk_tile(mt);
+      qk_post(mt - 1);
     }
+    qk_post(C::MT - 1);
 
     // ---- online softmax statistics in the log2 domain, one running-max update per key block
     mx = fmaxf(mx, __shfl_xor(mx, 32));
