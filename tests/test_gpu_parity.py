@@ -160,15 +160,18 @@ def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None, inputs=
 
 
 def _check_order(ws, L):
-    """The attention work order covers every (head, query block) exactly once, each die's slice
-    holding a contiguous share of every head."""
+    """The attention work order covers every (head, query block) exactly once; each die's slice
+    holds a block of every head with that die's share of the head's rows."""
     import torch
     Nb, BH = L["Nb"], L["bh"]
     stride = BH * -(-Nb // 8)
     tab = b.section(ws, L, "order", torch.int32, (8, stride)).cpu().numpy().view(np.uint32)
     seen = []
+    q, rem = divmod(Nb, 8)
     for x in range(8):
-        size = (x + 1) * Nb // 8 - x * Nb // 8
+        # snake deal of the cost-ranked rows: one row per die per round, the last partial round
+        # going to dies 0.. (even round count) or ..7 (odd)
+        size = q + int(x >= 8 - rem if q % 2 else x < rem)
         items = tab[x, :BH * size]
         assert np.all((items >> 16).reshape(BH, size) == np.arange(BH)[:, None])
         seen.append(items)

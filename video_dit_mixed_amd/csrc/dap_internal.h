@@ -56,10 +56,19 @@ struct Ws {
 // The cut of each level is found by an MSD radix select with 8 digits (7 x 11 bits + 10 bits).
 constexpr int kXcds = 8;  // MI355X: 8 accelerator dies, workgroups dispatched round-robin
 
-// Attention work slice of die x holds, for each head, rows [floor(x*Nb/8), floor((x+1)*Nb/8))
-// of that head's similarity order.
-__host__ __device__ inline int xcd_chunk_begin(int x, int Nb) { return (int)(((long long)x * Nb) / kXcds); }
-__host__ __device__ inline int xcd_chunk_size(int x, int Nb) { return xcd_chunk_begin(x + 1, Nb) - xcd_chunk_begin(x, Nb); }
+// Attention work slices: a head's rows, ranked by cost (most expensive first), are dealt to the
+// dies in snake order (rank i goes to die i % 8 in even rounds i / 8, to die 7 - i % 8 in odd
+// ones), so every die gets rows of every length and near-equal work.  Die x holds
+// xcd_chunk_size(x, Nb) rows of each head: one per round, plus one from the final partial round.
+__host__ __device__ inline int xcd_die_of_rank(int i) {
+  const int r = i / kXcds, p = i % kXcds;
+  return (r & 1) ? kXcds - 1 - p : p;
+}
+__host__ __device__ inline int xcd_chunk_size(int x, int Nb) {
+  const int q = Nb / kXcds, rem = Nb % kXcds;
+  const bool extra = (q & 1) ? (x >= kXcds - rem) : (x < rem);
+  return q + (extra ? 1 : 0);
+}
 __host__ __device__ inline int xcd_stride(int bh, int Nb) { return bh * ((Nb + kXcds - 1) / kXcds); }
 
 constexpr int kRankDigits = 8;

@@ -287,11 +287,13 @@ __global__ __launch_bounds__(256) void rank_assign_kernel(Geo g, const double* _
 }
 
 
-// Attention work order for one head (one workgroup): the head's query blocks are cut into 8
-// contiguous slices, one per accelerator die, and inside a slice the most expensive rows go first
-// (cost 3 per 16-bit pair, 2 per low-bit pair) so that long rows do not trail at the end of the
-// launch.  (Clustering rows with similar key lists onto a die raises its L2 hit rate but makes the
-// co-resident workgroups request the same tiles at the same moment, which measured slower.)
+// Attention work order for one head (one workgroup): the head's query blocks are ranked by cost
+// (3 per 16-bit pair, 2 per low-bit pair; ties by row) and dealt to the 8 accelerator dies in
+// snake order, so that each die's share of the head holds rows of every length and about an
+// eighth of the work.  A die runs its rows most expensive first, so long rows do not trail at the
+// end of the launch.  (Contiguous row ranges per die kept neighbouring rows on one die's L2 but
+// left the dies up to 6 % apart in work; clustering rows with similar key lists onto a die raised
+// its L2 hit rate but made co-resident workgroups request the same tiles at the same moment.)
 constexpr int kOrderThreads = 1024;
 
 __device__ void bitonic_sort_u64(unsigned long long* a, int n_pow2) {
@@ -319,38 +321,23 @@ __global__ __launch_bounds__(kOrderThreads) void rank_order_kernel(Geo g,
   const int bh = blockIdx.x, Nb = g.Nb;
   int n2 = 1;
   while (n2 < Nb) n2 <<= 1;
-  for (int qb = threadIdx.x; qb < n2; qb += blockDim.x) s_key[qb] = qb < Nb ? (unsigned long long)qb : ~0ull;
-  __syncthreads();
-  // second key: (slice, descending cost, row); computed into registers, then written back
-  unsigned long long k2[4096 / kOrderThreads];
-#pragma unroll
-  for (int t = 0; t < 4096 / kOrderThreads; ++t) {
-    const int i = threadIdx.x + t * kOrderThreads;
-    k2[t] = ~0ull;
-    if (i < Nb) {
-      const int qb = (int)(s_key[i] & 4095);
-      int x = 0;
-      while (x + 1 < kXcds && i >= xcd_chunk_begin(x + 1, Nb)) ++x;
+  // key: (descending cost, row); padding keys sort last
+  for (int qb = threadIdx.x; qb < n2; qb += blockDim.x) {
+    unsigned long long key = ~0ull;
+    if (qb < Nb) {
       const int32_t* cnt = counts + ((size_t)bh * Nb + qb) * 4;
       const int cost = 3 * cnt[0] + 2 * (cnt[1] + cnt[2]);  // <= 3 * 4096
-      k2[t] = ((unsigned long long)x << 40) | ((unsigned long long)(16383 - cost) << 16) | (unsigned)qb;
+      key = ((unsigned long long)(16383 - cost) << 16) | (unsigned)qb;
     }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < 4096 / kOrderThreads; ++t) {
-    const int i = threadIdx.x + t * kOrderThreads;
-    if (i < n2) s_key[i] = k2[t];
+    s_key[qb] = key;
   }
   __syncthreads();
   bitonic_sort_u64(s_key, n2);
   const int stride = xcd_stride(g.bh, Nb);
   for (int i = threadIdx.x; i < Nb; i += blockDim.x) {
-    const unsigned long long key = s_key[i];
-    const int x = (int)(key >> 40);
-    const int qb = (int)(key & 0xffff);
-    const int idx = i - xcd_chunk_begin(x, Nb);
-    order[(size_t)x * stride + (size_t)bh * xcd_chunk_size(x, Nb) + idx] = ((uint32_t)bh << 16) | (uint32_t)qb;
+    const int qb = (int)(s_key[i] & 0xffff);
+    const int x = xcd_die_of_rank(i);
+    order[(size_t)x * stride + (size_t)bh * xcd_chunk_size(x, Nb) + i / kXcds] = ((uint32_t)bh << 16) | (uint32_t)qb;
   }
 }
 
