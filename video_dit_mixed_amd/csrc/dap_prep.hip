@@ -15,7 +15,8 @@
 //                             byte = e + 127, code = E2M1 rne saturating of x*2^-e, sign = sign
 //                             bit of x; two codes per byte, even channel in the low nibble.
 //   FP8 V per (head, ch):     a_d = max|V[:, d]| over real tokens, r = 448/a_d,
-//                             code = e4m3fn rne saturating of x*r, scale = a_d/448.
+//                             code = e4m3fn rne of x*r (|x*r| <= 448, so no saturation case;
+//                             the hardware converter v_cvt_pk_fp8_f32), scale = a_d/448.
 // Launch shapes: prep_qk one 256-thread workgroup per (block, head, tensor); v_amax a grid of
 // token slices per head; v_pack one workgroup per (block, head).  Reads are whole region rows
 // (region_w * D * 2 contiguous bytes) with 16-byte lanes.
@@ -59,30 +60,6 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   if (amax == 0.0f || ef == 0) return -127;  // zero or subnormal: floor(log2) - 2 < -127
   int e = (int)ef - 127 - 2;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// fp32 -> e4m3fn byte, round to nearest even, saturating at 448; sign from the sign bit.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t bits = __float_as_uint(y);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float mag = fabsf(y);
-  uint32_t code;
-  if (mag >= 448.0f) {
-    code = 0x7e;
-  } else {
-    int E = (int)((bits >> 23) & 0xff) - 127;
-    if (E < -6) {
-      code = (uint32_t)rintf(mag * 512.0f);  // subnormal quantum 2^-9; 8 means 2^-6 (code 0x08)
-    } else {
-      uint32_t m = (uint32_t)rintf(ldexpf(mag, 3 - E));  // in [8, 16]
-      if (m == 16) {
-        E += 1;
-        m = 8;
-      }
-      code = ((uint32_t)(E + 7) << 3) | (m - 8);
-    }
-  }
-  return sign | code;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
