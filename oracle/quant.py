@@ -160,6 +160,36 @@ def mxfp4_decode(codes: np.ndarray, e8m0: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
+# NVFP4 (the pages' 4-bit example format; a comparison format, not on the GPU path)
+
+
+def nvfp4_dequant(x: np.ndarray) -> np.ndarray:
+    """NVFP4 round trip of rows x [..., D] (fp64 values of bf16): E2M1 elements in groups of 16
+    consecutive channels, each group scaled by an E4M3 factor, on top of one fp32 factor for the
+    whole tensor (pchao.org blog, section 方法概览 bullet 2: the low-bit level is, for example,
+    NVFP4).  Written from the two-level scaling the format defines:
+      s_t = amax(x) / (6 * 448)                        (fp64; the tensor's largest value maps to
+                                                        the largest element times the largest scale)
+      s_g = e4m3fn_rne_sat(amax(group) / (6 * s_t))    (group scale on the E4M3 grid)
+      v   = sign(x) * E2M1_rne_sat(|x| / step) * step,  step = s_g * s_t   (0 for a zero scale)
+    Returns the dequantised fp64 values (same shape)."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    amax_t = float(np.max(np.abs(x))) if x.size else 0.0
+    if amax_t == 0.0:
+        return np.zeros_like(x)
+    s_t = amax_t / (6.0 * 448.0)
+    xg = x.reshape(x.shape[:-1] + (D // 16, 16))
+    s_g = e4m3fn_rne_sat(np.max(np.abs(xg), axis=-1) / (6.0 * s_t))
+    step = s_g * s_t
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scaled = np.where(step[..., None] > 0, np.abs(xg) / step[..., None], 0.0)
+    mag = E2M1_GRID[e2m1_rne_sat(scaled)]
+    v = np.where(np.signbit(xg), -mag, mag) * step[..., None]
+    return v.reshape(x.shape)
+
+
+# ----------------------------------------------------------------------------------------------
 # FP8 V per channel
 
 

@@ -15,7 +15,8 @@ a 4-bit pair 1/10.1 + 1/5).
   gpu leg  the HIP path through the C ABI at a full-size layer; the error is taken on a sample of
            query rows of several heads, against the oracle's exact dense rows (fp64).
   cpu leg  the oracle alone (phased attention with its emulated roundings) on a reduced layer with
-           the same block geometry, against exact dense attention over every row.
+           the same block geometry, against exact dense attention over every row; --fp4 nvfp4
+           swaps the 4-bit level's MXFP4 Q/K for NVFP4 (the pages' example format) to compare.
 
 rel-L2 = ||O - O_dense||_2 / ||O_dense||_2 over the rows taken; the bf16 rounding of the output
 alone gives about 1.1e-3.
@@ -146,7 +147,7 @@ def gpu_leg(args):
 
 
 def cpu_leg(args):
-    from oracle import pipeline
+    from oracle import pipeline, quant
     # same 8x16-region, 128-token block geometry as the full-size layers, smaller latent
     w = synth.Workload("quality_small_4x24x48", 4, 24, 48, 2, 128, 8, 16, 0.5,
                        (8500, 0, 750, 750), seed=2024)
@@ -161,12 +162,16 @@ def cpu_leg(args):
         got, exp = [], []
         for bh in range(w.batch * w.heads):
             b_, h_ = divmod(bh, w.heads)
-            r = pipeline.run_head(Q[b_, h_], K[b_, h_], V[b_, h_], T=w.T, H=w.H, W=w.W,
-                                  rh=w.region_h, rw=w.region_w, lam=lam, quota_bp=tuple(quota))
-            got.append(r.out_bf16())
+            r = pipeline.prepare_head(Q[b_, h_], K[b_, h_], V[b_, h_], T=w.T, H=w.H, W=w.W,
+                                      rh=w.region_h, rw=w.region_w, lam=lam, quota_bp=tuple(quota))
+            if args.fp4 == "nvfp4":
+                # the pages' 4-bit example format in place of MXFP4 (same map, same other levels)
+                r.q_fp4_val = quant.nvfp4_dequant(r.qp)
+                r.k_fp4_val = quant.nvfp4_dequant(r.kp)
+            got.append(pipeline.attend(r).out_bf16())
             exp.append(ref[bh])
         r2, mabs = rel(np.concatenate(got), np.concatenate(exp))
-        r = {"leg": "cpu-oracle", "workload": w.name, "allocation": name,
+        r = {"leg": "cpu-oracle", "fp4": args.fp4, "workload": w.name, "allocation": name,
              "quota_bp_skip_4_8_16": list(quota), "lambda": lam,
              "t_roof_units_per_bp": round(budget(quota), 2), "rel_l2": round(r2, 5),
              "max_abs": round(mabs, 4), "oracle_s": round(time.perf_counter() - t0, 1)}
@@ -184,6 +189,8 @@ def main():
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--seed", type=int, default=77)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--fp4", choices=["mxfp4", "nvfp4"], default="mxfp4",
+                    help="cpu leg: the 4-bit format of Q and K (the GPU path implements MXFP4)")
     args = ap.parse_args()
     res = gpu_leg(args) if args.leg == "gpu" else cpu_leg(args)
     if args.out:

@@ -187,3 +187,45 @@ def test_fp8_v_channel_scale_and_zero_channel():
     big = np.abs(vp) > np.max(np.abs(v), axis=0) * 2.0 ** -6
     assert np.all(np.abs(deq - vp)[big] <= np.abs(vp)[big] * 2.0 ** -4 * 1.0001)
     assert not codes[100:].any()
+
+
+def test_nvfp4_matches_brute_force_nearest_grid_point():
+    """Each NVFP4 value is the nearest point of its group's grid {+-E2M1 * step}, step = s_g s_t
+    (ties to the even code), with s_g the E4M3 rounding of amax/(6 s_t); found here by exhaustive
+    search."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((6, 64)) * np.exp(rng.uniform(-4, 4, (6, 1)))).astype(np.float64)
+    x[2, 16:32] = 0.0                       # an all-zero group
+    x[3, 5] = 40.0                          # an outlier sets the tensor scale
+    got = quant.nvfp4_dequant(x)
+    s_t = np.abs(x).max() / (6 * 448)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for r in range(x.shape[0]):
+        for g in range(4):
+            blk = x[r, 16 * g:16 * g + 16]
+            s_g = quant.e4m3fn_rne_sat(np.array([np.abs(blk).max() / (6 * s_t)]))[0]
+            for i, v in enumerate(blk):
+                if s_g == 0:
+                    assert got[r, 16 * g + i] == 0.0
+                    continue
+                cand = grid * (s_g * s_t)      # the group's grid: E2M1 values times its step
+                d = np.abs(np.abs(v) - cand)
+                best = np.flatnonzero(d == d.min())
+                k = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+                exp = np.copysign(cand[k], v) if cand[k] != 0 else (np.copysign(0.0, v))
+                assert got[r, 16 * g + i] == exp, (r, g, i, v, got[r, 16 * g + i], exp)
+
+
+def test_nvfp4_exact_on_representable_values_and_saturates():
+    # values already on a group's grid come back unchanged: pick s_t from the tensor max, a group
+    # scale on the e4m3 grid, elements on the E2M1 grid
+    s_t = 6.0 / (6 * 448)                     # tensor max 6 -> s_t = 1/448
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    row = np.concatenate([grid, -grid[::-1]]) * 448 * s_t   # group scale 448 (largest) -> max 6
+    x = np.stack([row, row * 0.5])            # second group: scale 224 (on the e4m3 grid)
+    np.testing.assert_array_equal(quant.nvfp4_dequant(x), x)
+    # the largest element of every group maps to at most 6 * s_g * s_t
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((4, 32))
+    v = quant.nvfp4_dequant(y)
+    assert np.all(np.abs(v) <= np.abs(y).max() * (1 + 2 ** -3) + 1e-12)
