@@ -19,10 +19,14 @@
 // One fp32 accumulator serves all phases.  At the first low-bit block its channel d is converted
 // to low-bit units (x 2^8 / s_V[d]); the end multiplies by s_V[d] 2^-8 and divides by l.
 // Key and V tiles are staged through LDS in an XOR-swizzled layout (bank-conflict-free reads).
-// Global loads run ahead in registers: a tile's V loads are issued before its Q K^T and stored to
-// LDS just before its P V; the next tile's K loads are issued before the P V products and stored
-// at the top of the next iteration.  The matrix-core operand
-// orders were fixed when the operands were packed, so every LDS read is one or two 16-byte loads.
+// For 128-token blocks the load unit writes them into LDS directly (buffer loads with an LDS
+// destination), so no registers hold them on the way; smaller blocks stage them through
+// registers.  A tile's V is issued at the top of its iteration and lands during Q K^T and the
+// softmax; the next tile's K is issued as the P V products start and lands before the next
+// Q K^T.  The matrix-core operand orders were fixed when the operands were packed, so every LDS
+// read is one or two 16-byte loads.
+#include <type_traits>
+
 #include "dap_internal.h"
 
 namespace dap {
@@ -52,6 +56,9 @@ struct AttnCfg {
   static constexpr int KBYTES = KT * 2 * D;        // largest key tile (bf16)
   static constexpr int SBYTES = 64 * NW * 4;       // E8M0 key scales (one 4-byte DMA per wave)
   static constexpr int VBYTES = (D * 2 * B > D * KP8) ? D * 2 * B : D * KP8;
+  // Tiles go straight to LDS for 128-token blocks; smaller blocks (more tile bytes per flop) were
+  // measured faster with the tiles staged through registers.
+  static constexpr bool DIRECT = B >= 128;
 };
 
 // Per-phase tile geometry.  PH = 0: bf16 K rows / bf16 V^T rows; 1: int8 K / e4m3 V^T;
@@ -108,34 +115,55 @@ __device__ __forceinline__ int list_at(const RowCtx& c, int i) {
   return (int)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
 }
 
-// One key block's operand tile held in registers between its global load and its LDS store.
-// Slot s (16 bytes) of a tile of rows with RC chunks sits at LDS byte 16*s and holds row s / RC,
-// logical chunk (s % RC) ^ swizzle; thread t owns slots t, t + NT, t + 2*NT, ...
-template <int ROWS, int RC, int NT>
-struct TileRegs {
-  static constexpr int N = ROWS * RC / NT;
+// Moves one key block's operand tile from global memory into LDS.  Slot s (16 bytes) of a tile of
+// rows with RC chunks sits at LDS byte 16*s and holds row s / RC, logical chunk (s % RC) ^ swizzle;
+// thread t fills slots t, t + NT, t + 2*NT, ...  The loads are buffer loads with a wave-uniform
+// resource and a 32-bit offset per lane (a 64-bit address per lane costs more to issue); rows >=
+// valid fall outside the resource's range and read as zero.
+//   kDirect: the load unit writes LDS itself (buffer loads with an LDS destination).  One
+//     wave-level load writes 1 KB contiguous at a wave-uniform base, lane l at base + 16 l, which
+//     is why the swizzle is applied on the global side.  No registers hold the tile; completion is
+//     counted by vmcnt, in issue order, and commit() does nothing.
+//   otherwise: the tile is held in registers from load() until commit() stores it.
+template <int ROWS, int RC, int NT, bool kDirect>
+struct TileMover {
+  static constexpr int N = ROWS * RC / NT;  // 16-byte loads per thread
   static_assert(ROWS * RC % NT == 0, "tile must split evenly over the threads");
-  uint4 v[N];
+  uint4 v[kDirect ? 1 : N];
 
-  // Buffer loads: a wave-uniform resource for the tile plus a 32-bit offset per lane (a 64-bit
-  // address per lane costs more to issue), and rows >= valid fall outside the resource's range,
-  // which reads as zero.
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ gsrc, int valid, int tid) {
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ gsrc, int valid, int tid, uint8_t* lds) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(gsrc), (short)0, valid * RC * 16, kRsrcWord3);
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int sl = tid + j * NT;
       const int r = sl / RC, pc = sl - (sl / RC) * RC;
-      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, r * (RC * 16) + 16 * swz<RC>(r, pc), 0, 0);
-      v[j] = make_uint4(t[0], t[1], t[2], t[3]);
+      const int off = r * (RC * 16) + 16 * swz<RC>(r, pc);
+      if constexpr (kDirect) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(lds + 16 * (64 * wv + j * NT)), 16, off, 0, 0, 0);
+      } else {
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        v[j] = make_uint4(t[0], t[1], t[2], t[3]);
+      }
     }
   }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+  __device__ __forceinline__ void commit(uint8_t* lds, int tid) const {
+    if constexpr (!kDirect) {
 #pragma unroll
-    for (int j = 0; j < N; ++j) *reinterpret_cast<uint4*>(lds + 16 * (tid + j * NT)) = v[j];
+      for (int j = 0; j < N; ++j) *reinterpret_cast<uint4*>(lds + 16 * (tid + j * NT)) = v[j];
+    }
   }
 };
+
+// Wait until at most N of this wave's vector-memory loads are outstanding (s_waitcnt with the
+// export and LDS counters left at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
 
 // Workgroup barrier without a memory fence (LDS traffic is ordered by lgkmcnt; global loads that
 // are still in flight belong to the next tile and must not be waited for here).
@@ -185,14 +213,14 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
   if (PH == 1) s_q = __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(w.q_i8_scale) + (size_t)c.bh * g.Nb + c.qb));
   using P = PhaseCfg<B, D, PH>;
   const int lane = c.tid & 63;
-  TileRegs<C::KT, P::KRC, C::NT> kreg;
-  TileRegs<D, P::VRC, C::NT> vreg;
+  TileMover<C::KT, P::KRC, C::NT, C::DIRECT> kt;
+  TileMover<D, P::VRC, C::NT, C::DIRECT> vt;
   uint32_t kscale = 0;  // E8M0 key scales of the staged tile (4-bit phase), 4 bytes per thread
 
-  // prologue: the first key block's tiles go to registers
+  // prologue: the first key block's K is loaded
   {
     const int kb0 = list_at(c, off);
-    kreg.load(k_tile_src<B, D, PH>(g, w, c.bh, kb0), B, c.tid);
+    kt.load(k_tile_src<B, D, PH>(g, w, c.bh, kb0), B, c.tid, sK);
     if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
       kscale = c.tid < B * (D / 32) / 4
                    ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb0 * B) * (D / 32) + 4 * c.tid)
@@ -209,14 +237,15 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     const int vh = min(g.rh, g.H - ry * g.rh), vw = min(g.rw, g.W - rx * g.rw);
     const bool full = vh == g.rh && vw == g.rw && B == C::KT;
     bar();  // every wave is done with the previous tile's sK / sV / sBias
-    kreg.store(sK, c.tid);
-    // this tile's V streams into registers while Q K^T and the softmax run
-    vreg.load(v_tile_src<B, D, PH>(g, w, c.bh, kb), D, c.tid);
+    kt.commit(sK, c.tid);
+    // this tile's V streams in while Q K^T and the softmax run
+    vt.load(v_tile_src<B, D, PH>(g, w, c.bh, kb), D, c.tid, sV);
     if (PH == 2 && c.tid < C::KT * (D / 32) / 4) *reinterpret_cast<uint32_t*>(sKs + 4 * c.tid) = kscale;
     if (!full && c.tid < C::KT) {
       const int m = c.tid, iy = m / g.rw, ix = m - (m / g.rw) * g.rw;
       sBias[m] = (m < B && iy < vh && ix < vw) ? 0.0f : -INFINITY;
     }
+    if constexpr (C::DIRECT) wait_vm<decltype(vt)::N>();  // K (issued one tile earlier) has landed
     bar();
     // per-lane LDS addresses are recomputed in every iteration (a few integer ops) instead of
     // being hoisted out of the loop, where they would pin dozens of registers
@@ -267,13 +296,16 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         S[mt] = acc;
       }
     };
-    auto qk_post = [&](int mt) {
+    // kFull: the block has no padding keys, known at compile time (low-bit phases) or at run
+    // time (16-bit phase)
+    auto qk_post = [&](int mt, auto full_c) {
+      constexpr bool kFull = decltype(full_c)::value;
       if (PH == 1) {
         const i32x16 si = __builtin_bit_cast(i32x16, S[mt]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[mt][r] = (float)si[r];
       }
-      if (full) {
+      if (kFull || (PH == 0 && full)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
       } else {
@@ -292,13 +324,23 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     };
     // one m-tile of lookahead: the products of m-tile mt are issued before m-tile mt - 1's
     // conversion and maximum, which then run while the matrix core works
-    qk_tile(0);
+    auto qk_all = [&](auto full_c) {
+      qk_tile(0);
 #pragma unroll
-    for (int mt = 1; mt < C::MT; ++mt) {
-      qk_tile(mt);
-      qk_post(mt - 1);
-    }
-    qk_post(C::MT - 1);
+      for (int mt = 1; mt < C::MT; ++mt) {
+        qk_tile(mt);
+        qk_post(mt - 1, full_c);
+      }
+      qk_post(C::MT - 1, full_c);
+    };
+    // Low-bit phases take the full / edge choice once per key block, so each copy of the pipeline
+    // is straight-line code in which the scheduler can interleave products, conversions and
+    // maxima.  The 16-bit phase keeps the choice per m-tile: two copies of it do not fit in the
+    // registers.
+    if (PH != 0 && full)
+      qk_all(std::true_type{});
+    else
+      qk_all(std::false_type{});
 
     // ---- online softmax statistics in the log2 domain, one running-max update per key block
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -315,14 +357,14 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
         for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
     }
 
-    // ---- O^T += V^T P^T.  V goes to LDS first; the next key block's K streams into registers
-    // during the products (the load is unconditional -- the last tile re-reads its own block --
-    // so the staging registers are dead between the store at the top and this point).  P is
+    // ---- O^T += V^T P^T.  Once V is in LDS and every wave is past its Q K^T, the next key
+    // block's K streams in during the products.  P is
     // produced chunk by chunk right before the products that consume it, so its exponentials
     // can run under the previous chunk's matrix-core work.
-    vreg.store(sV, c.tid);
-    bar();
-    kreg.load(k_tile_src<B, D, PH>(g, w, c.bh, kb_next), B, c.tid);
+    if constexpr (C::DIRECT) wait_vm<0>();
+    vt.commit(sV, c.tid);
+    bar();  // V visible; every wave is done with sK
+    if (it + 1 < np) kt.load(k_tile_src<B, D, PH>(g, w, c.bh, kb_next), B, c.tid, sK);
     if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
       kscale = c.tid < B * (D / 32) / 4
                    ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb_next * B) * (D / 32) + 4 * c.tid)
