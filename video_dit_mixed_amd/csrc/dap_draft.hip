@@ -6,9 +6,9 @@
 // Figure 2 caption.  fp64 keeps the scores exact enough that the per-head ranking (and so the block
 // map) is reproducible bit for bit.
 //
-// Kernels: draft_logits -- a 128x128-tile fp64 GEMM per (head, map), writing L_avg into the score
-// buffer and L_max into a scratch buffer; draft_mix -- one workgroup per query region row,
-// exponentials staged in LDS, writes A over L_avg.
+// Kernels: draft_logits -- a 128x128-tile fp64 GEMM per (head, map) on the fp64 matrix cores,
+// writing L_avg into the score buffer and L_max into a scratch buffer; draft_mix -- one workgroup
+// per query region row, exponentials staged in LDS, writes A over L_avg.
 #pragma clang fp contract(off)
 
 #include "dap_internal.h"
@@ -18,69 +18,84 @@ namespace {
 
 constexpr int kTile = 128;  // output tile edge (rows and columns of one workgroup)
 constexpr int kKc = 16;     // channels staged per step
+constexpr int kPitch = kKc + 2;  // LDS row pitch in doubles (see the fragment reads below)
 
-// 256 threads, each an 8 x 8 block of outputs (rows 8 ty + i; columns 2 tx + 32 jj + e, jj < 4,
-// e < 2): per channel a thread reads its 8 Q values and 8 K values as four 16-byte LDS loads each
-// (the K loads of 16 neighbouring threads are contiguous, so bank-conflict free) and does 64 fused
-// multiply-adds.  Each output is one fma chain over the channels in ascending order.
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
+// fp64 matrix cores (v_mfma_f64_16x16x4_f64): 4 waves, wave (wr, wc) owns the 64 x 64 outputs
+// rows 64 wr.., columns 64 wc.. of the tile as 4 x 4 MFMA tiles of 16 x 16.  Per 4 channels an
+// MFMA takes A[m][k] = Qbar[row m][channel k] from lane m + 16 k and B[k][n] = Kbar[col n][channel
+// k] from lane n + 16 k, and accumulates D[m][n] = sum_k A[m][k] B[k][n] in fp64; lane l holds
+// D[4 e + l / 16][l % 16] in element e.  Operands are staged through LDS in row-major tiles with a
+// pitch of 18 doubles: the 16 rows x 2 channels of a half-wave read land in 32 distinct bank pairs.
+// The products of each MFMA are accumulated in channel order with fused multiply-adds, so every
+// logit equals one fma chain over the channels in ascending order (measured bit for bit against a
+// vector-FMA version of this kernel).  Two waves per SIMD: 179 VGPRs.
 template <int D>
-__global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, Ws w) {
-  __shared__ __attribute__((aligned(16))) double sQ[kKc][kTile + 2];
-  __shared__ __attribute__((aligned(16))) double sK[kKc][kTile + 2];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void draft_logits_kernel(Geo g, Ws w) {
+  __shared__ __attribute__((aligned(16))) double sQ[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) double sK[kTile * kPitch];
   const int bh = blockIdx.z >> 1, which = blockIdx.z & 1;
   const double* qbar = (which == 0 ? w.q_avg : w.q_max) + (size_t)bh * g.Nb * D;
   const double* kbar = (which == 0 ? w.k_avg : w.k_max) + (size_t)bh * g.Nb * D;
   double* dst = (which == 0 ? w.scores : w.lmax) + (size_t)bh * g.pairs;
   const int row0 = blockIdx.y * kTile, col0 = blockIdx.x * kTile;
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  double acc[8][8];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wr = wv >> 1, wc = wv & 1;
+  const int li = lane & 15, lk = lane >> 4;
+  // staging: thread t copies 8 channels (one 64-byte run) of row t / 2 of each operand
+  const int sr = tid >> 1, sc = 8 * (tid & 1);
+  const int qr = row0 + sr, kr = col0 + sr;
+  f64x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   for (int d0 = 0; d0 < D; d0 += kKc) {
-    // 128 rows x 16 channels of each operand: 2048 values, 8 per thread
+    double2 qv[4], kv[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + i * 256;
-      const int r = e / kKc, c = e % kKc;
-      const int qr = row0 + r, kr = col0 + r;
-      sQ[c][r] = qr < g.Nb ? qbar[(size_t)qr * D + d0 + c] : 0.0;
-      sK[c][r] = kr < g.Nb ? kbar[(size_t)kr * D + d0 + c] : 0.0;
+    for (int e = 0; e < 4; ++e) {
+      qv[e] = qr < g.Nb ? *reinterpret_cast<const double2*>(qbar + (size_t)qr * D + d0 + sc + 2 * e)
+                        : double2{0.0, 0.0};
+      kv[e] = kr < g.Nb ? *reinterpret_cast<const double2*>(kbar + (size_t)kr * D + d0 + sc + 2 * e)
+                        : double2{0.0, 0.0};
+    }
+    __syncthreads();  // every wave is done with the previous channels
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<double2*>(sQ + sr * kPitch + sc + 2 * e) = qv[e];
+      *reinterpret_cast<double2*>(sK + sr * kPitch + sc + 2 * e) = kv[e];
     }
     __syncthreads();
-#pragma unroll 2
-    for (int c = 0; c < kKc; ++c) {
-      double a[8], b[8];
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const double2 qa = *reinterpret_cast<const double2*>(&sQ[c][8 * ty + i]);
-        const double2 kb = *reinterpret_cast<const double2*>(&sK[c][2 * tx + 16 * i]);
-        a[i] = qa.x;
-        a[i + 1] = qa.y;
-        b[i] = kb.x;
-        b[i + 1] = kb.y;
+    for (int k4 = 0; k4 < kKc; k4 += 4) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = sQ[(64 * wr + 16 * i + li) * kPitch + k4 + lk];
+        b[i] = sK[(64 * wc + 16 * i + li) * kPitch + k4 + lk];
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
   }
   const double inv_sq = 1.0 / sqrt((double)D);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = row0 + 8 * ty + i;
-    if (r >= g.Nb) continue;
-    double* drow = dst + (size_t)r * g.Nb;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = col0 + 2 * tx + 16 * (j & ~1) + (j & 1);  // b[j] of column 2 tx + 32 (j/2) + j%2
-      if (col < g.Nb) drow[col] = acc[i][j] * inv_sq;
+    for (int e = 0; e < 4; ++e) {
+      const int r = row0 + 64 * wr + 16 * i + 4 * e + lk;
+      if (r >= g.Nb) continue;
+      double* drow = dst + (size_t)r * g.Nb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = col0 + 64 * wc + 16 * j + li;
+        if (col < g.Nb) drow[col] = acc[i][j][e] * inv_sq;
+      }
     }
-  }
 }
 
 __device__ double block_reduce(double v, bool is_max, double* s_red) {
