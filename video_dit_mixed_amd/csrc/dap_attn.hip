@@ -236,17 +236,20 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     const int ry = rem / g.nbx, rx = rem - ry * g.nbx;
     const int vh = min(g.rh, g.H - ry * g.rh), vw = min(g.rw, g.W - rx * g.rw);
     const bool full = vh == g.rh && vw == g.rw && B == C::KT;
-    bar();  // every wave is done with the previous tile's sK / sV / sBias
+    // Two barriers per key block.  sK, sKs and sBias were last read by the previous Q K^T, which
+    // every wave finished before the barrier ahead of the previous P V, so they are written here
+    // without a barrier of their own; sV is free once every wave reaches the barrier below.
     kt.commit(sK, c.tid);
-    // this tile's V streams in while Q K^T and the softmax run
-    vt.load(v_tile_src<B, D, PH>(g, w, c.bh, kb), D, c.tid, sV);
+    if constexpr (!C::DIRECT) vt.load(v_tile_src<B, D, PH>(g, w, c.bh, kb), D, c.tid, sV);
     if (PH == 2 && c.tid < C::KT * (D / 32) / 4) *reinterpret_cast<uint32_t*>(sKs + 4 * c.tid) = kscale;
     if (!full && c.tid < C::KT) {
       const int m = c.tid, iy = m / g.rw, ix = m - (m / g.rw) * g.rw;
       sBias[m] = (m < B && iy < vh && ix < vw) ? 0.0f : -INFINITY;
     }
-    if constexpr (C::DIRECT) wait_vm<decltype(vt)::N>();  // K (issued one tile earlier) has landed
-    bar();
+    if constexpr (C::DIRECT) wait_vm<0>();  // K (issued one key block earlier) has landed
+    bar();  // K, scales and bias visible; every wave is done with the previous P V
+    // this tile's V streams in while Q K^T and the softmax run
+    if constexpr (C::DIRECT) vt.load(v_tile_src<B, D, PH>(g, w, c.bh, kb), D, c.tid, sV);
     // per-lane LDS addresses are recomputed in every iteration (a few integer ops) instead of
     // being hoisted out of the loop, where they would pin dozens of registers
     int ln = lane;
