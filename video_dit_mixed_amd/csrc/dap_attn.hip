@@ -21,10 +21,10 @@
 // Key and V tiles are staged through LDS in an XOR-swizzled layout (bank-conflict-free reads).
 // For 128-token blocks the load unit writes them into LDS directly (buffer loads with an LDS
 // destination), so no registers hold them on the way; smaller blocks stage them through
-// registers.  A tile's V is issued at the top of its iteration and lands during Q K^T and the
-// softmax; the next tile's K is issued as the P V products start and lands before the next
-// Q K^T.  The matrix-core operand orders were fixed when the operands were packed, so every LDS
-// read is one or two 16-byte loads.
+// registers.  Two barriers per key block: after the first, the tile's V is issued and lands
+// during Q K^T and the softmax; after the second, the next tile's K is issued and lands during
+// the P V products.  The matrix-core operand orders were fixed when the operands were packed, so
+// every LDS read is one or two 16-byte loads.
 #include <type_traits>
 
 #include "dap_internal.h"
@@ -54,11 +54,12 @@ struct AttnCfg {
   static constexpr int DT = D / 32;                // O^T m-tiles (32 channels each)
   static constexpr int KP8 = (B + 63) / 64 * 64;   // FP8 V^T row length
   static constexpr int KBYTES = KT * 2 * D;        // largest key tile (bf16)
-  static constexpr int SBYTES = 64 * NW * 4;       // E8M0 key scales (one 4-byte DMA per wave)
+  static constexpr int SBYTES = 64 * NW * 4;       // room for one tile's E8M0 key scales
   static constexpr int VBYTES = (D * 2 * B > D * KP8) ? D * 2 * B : D * KP8;
   // Tiles go straight to LDS for 128-token blocks; smaller blocks (more tile bytes per flop) were
   // measured faster with the tiles staged through registers.
   static constexpr bool DIRECT = B >= 128;
+  static_assert(KT * D / 32 <= SBYTES, "a tile's E8M0 key scales fit in sKs");
 };
 
 // Per-phase tile geometry.  PH = 0: bf16 K rows / bf16 V^T rows; 1: int8 K / e4m3 V^T;
@@ -361,9 +362,9 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     }
 
     // ---- O^T += V^T P^T.  Once V is in LDS and every wave is past its Q K^T, the next key
-    // block's K streams in during the products.  P is
-    // produced chunk by chunk right before the products that consume it, so its exponentials
-    // can run under the previous chunk's matrix-core work.
+    // block's K streams in during the products.  P is produced chunk by chunk right before the
+    // products that consume it, so its exponentials can run under the previous chunk's
+    // matrix-core work.
     if constexpr (C::DIRECT) wait_vm<0>();
     vt.commit(sV, c.tid);
     bar();  // V visible; every wave is done with sK
