@@ -53,6 +53,10 @@ def _cfg(**kw):
     (dict(batch=0), b.DAP_E_INVALID),
     (dict(T=0), b.DAP_E_INVALID),
     (dict(T=200, H=48, W=96, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),   # > 4096 regions
+    # extreme grids: rejected, with no 32-bit overflow on the way (H + region_h - 1, T * nby * nbx)
+    (dict(T=1, H=2**31 - 1, W=16, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),
+    (dict(T=2**31 - 1, H=2**31 - 1, W=2**31 - 1, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),
+    (dict(T=4097, H=8, W=16, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),
 ])
 def test_validation_rejects(kw, status):
     with pytest.raises(b.DapError) as e:

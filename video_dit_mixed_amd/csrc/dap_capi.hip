@@ -28,8 +28,11 @@ dap_status validate(const dap_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return DAP_E_UNSUPPORTED;
   const long long B = (long long)c->region_h * c->region_w;
   if (B != 16 && B != 64 && B != 128) return DAP_E_UNSUPPORTED;
-  const long long nby = (c->H + c->region_h - 1) / c->region_h;
-  const long long nbx = (c->W + c->region_w - 1) / c->region_w;
+  // widened before any arithmetic, and each factor bounded before the product, so that no
+  // configuration overflows on its way to the check
+  const long long nby = ((long long)c->H + c->region_h - 1) / c->region_h;
+  const long long nbx = ((long long)c->W + c->region_w - 1) / c->region_w;
+  if (c->T > 4096 || nby > 4096 || nbx > 4096) return DAP_E_UNSUPPORTED;
   const long long Nb = (long long)c->T * nby * nbx;
   if (Nb > 4096) return DAP_E_UNSUPPORTED;  // pair index must fit 24 bits; lists are uint16
   const long long bh = (long long)c->batch * c->heads;
