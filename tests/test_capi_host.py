@@ -131,3 +131,26 @@ def test_binding_refuses_missing_library(tmp_path):
             b.load(str(tmp_path / "nope.so"))
         finally:
             b._lib = saved
+
+
+def test_binding_checks_tensors_before_the_library_call():
+    """The kernels read q/k/v/out as contiguous bf16 [batch, heads, N, D] buffers; the binding
+    refuses anything else on the host (checked here with host tensors, before any device call)."""
+    import torch
+    cfg = _cfg()
+    shape = (cfg.batch, cfg.heads, cfg.N, cfg.head_dim)
+    good = torch.zeros(shape, dtype=torch.bfloat16)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    cases = [
+        (torch.zeros(shape, dtype=torch.float16), "dtype"),
+        (torch.zeros(shape[:-1] + (shape[-1] + 2,), dtype=torch.bfloat16)[..., :shape[-1]], "contiguous"),
+        (torch.zeros((cfg.batch * cfg.heads, cfg.N, cfg.head_dim), dtype=torch.bfloat16), "shape"),
+        (good, "device"),
+    ]
+    for q, what in cases:
+        with pytest.raises(ValueError, match=what):
+            b.prepare(cfg, q, good, good, ws)
+    with pytest.raises(ValueError, match="shape"):
+        b.restore(cfg, ws, torch.zeros((1, 1), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="bytes"):
+        b.draft_rank(cfg, ws, map_out=torch.zeros(3, dtype=torch.uint8))

@@ -152,6 +152,13 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr() if hasattr(t, "data_ptr") else int(t)
 
 
+def _prod(xs) -> int:
+    n = 1
+    for x in xs:
+        n *= int(x)
+    return n
+
+
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
@@ -163,25 +170,63 @@ def _stream(stream) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _expect(t, name: str, dtype: str, shape=None, min_bytes: int = 0):
+    """Host-side check of a torch tensor handed to the library as a bare pointer: the kernels
+    assume a contiguous device buffer of exactly this element type and size.  Integers (raw device
+    pointers) are passed through unchecked, as the C ABI takes them."""
+    if t is None or not hasattr(t, "data_ptr"):
+        return
+    import torch
+    want = getattr(torch, dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype != "uint8" and t.dtype != want:
+        raise ValueError(f"{name}: expected dtype {want}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_bytes and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name}: expected at least {min_bytes} bytes")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a device tensor, got device {t.device}")
+
+
+def _io_shape(cfg: Config):
+    return (cfg.batch, cfg.heads, cfg.N, cfg.head_dim)
+
+
+def _pairs_shape(cfg: Config):
+    nb = cfg.T * -(-cfg.H // cfg.region_h) * -(-cfg.W // cfg.region_w)
+    return (cfg.batch * cfg.heads, nb, nb)
+
+
 def prepare(cfg: Config, q, k, v, ws, stream=None):
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, name, "bfloat16", _io_shape(cfg))
+    _expect(ws, "ws", "uint8")
     c = cfg.c_struct()
     _check(load().dap_prepare(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(ws), _nbytes(ws),
                               _stream(stream)), "dap_prepare")
 
 
 def draft_rank(cfg: Config, ws, map_out=None, scores_out=None, stream=None):
+    _expect(map_out, "map_out", "uint8", min_bytes=_prod(_pairs_shape(cfg)))
+    _expect(scores_out, "scores_out", "float64", _pairs_shape(cfg))
+    _expect(ws, "ws", "uint8")
     c = cfg.c_struct()
     _check(load().dap_draft_rank(ctypes.byref(c), _ptr(ws), _nbytes(ws), _ptr(map_out),
                                  _ptr(scores_out), _stream(stream)), "dap_draft_rank")
 
 
 def attention(cfg: Config, ws, stream=None):
+    _expect(ws, "ws", "uint8")
     c = cfg.c_struct()
     _check(load().dap_attention(ctypes.byref(c), _ptr(ws), _nbytes(ws), _stream(stream)),
            "dap_attention")
 
 
 def restore(cfg: Config, ws, out, stream=None):
+    _expect(out, "out", "bfloat16", _io_shape(cfg))
+    _expect(ws, "ws", "uint8")
     c = cfg.c_struct()
     _check(load().dap_restore(ctypes.byref(c), _ptr(ws), _nbytes(ws), _ptr(out), _stream(stream)),
            "dap_restore")
