@@ -341,6 +341,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quota", default=None,
+                    help="override the workload's quotas: skip,4-bit,8-bit,16-bit in basis points "
+                         "(for per-phase counter runs; the traffic figure is then not reported)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (a kernel of known "
                          "read/write size for scaling HBM byte counters)")
@@ -352,8 +355,8 @@ def main():
     ap.add_argument("--out", default=None, help="--sweep: also write the JSON lines here")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the operator is per-head "
-              f"and this build measures one GPU's share; multi-GPU head sharding is not built.",
+        print(f"bench.py measures one GPU (got --gpus {args.gpus}): the operator shards by heads "
+              f"with no communication inside it, and the multi-GPU path is not implemented.",
               file=sys.stderr)
         sys.exit(2)
     if args.sweep:
@@ -368,6 +371,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w = synth.workload(args.workload)
+    if args.quota:
+        w = w.with_(quota_bp=tuple(int(x) for x in args.quota.split(",")))
     cfg = b.Config.from_workload(w)
     L = b.workspace_layout(cfg)
     t_gen = time.perf_counter()
@@ -416,7 +421,7 @@ def main():
     t_attn = statistics.mean(per["attention"]) * 1e-3
     achieved = flops / t_attn
     peak = flops / t_roof
-    traffic = read_traffic(w.name)
+    traffic = read_traffic(w.name) if not args.quota else None
     dtype = "/".join(x for x, n in (("bf16", n16), ("i8+fp8", n8), ("mxfp4+fp8", n4)) if n > 0)
 
     res = {
