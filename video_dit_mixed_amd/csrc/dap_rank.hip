@@ -82,6 +82,17 @@ __global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(Geo g, Ws w, co
     any |= active[j];
   }
   if (!any) return;
+  // Cuts that share a prefix (all three on the first pass) share one histogram: src[j] is the
+  // first active cut with cut j's prefix.  The scores of a head cluster in few top-digit bins, so
+  // every avoided LDS atomic is a contended one.
+  int src[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    src[j] = j;
+#pragma unroll
+    for (int k = 0; k < j; ++k)
+      if (src[j] == j && active[k] && active[j] && prefix[k] == prefix[j]) src[j] = k;
+  }
   // candidate mode: after the compaction, unless this head's list overflowed
   const long long ncand = pass > kCompactPass ? (long long)st[bh * 3].pad : -1;
   const bool cand = ncand >= 0 && ncand <= cand_cap(g);
@@ -104,13 +115,14 @@ __global__ __launch_bounds__(kHistThreads) void rank_hist_kernel(Geo g, Ws w, co
     const uint32_t digit = (uint32_t)(key >> shift) & mask;
 #pragma unroll
     for (int j = 0; j < 3; ++j)
-      if (active[j] && hi == prefix[j]) atomicAdd(&s_h[j][digit], 1u);
+      if (active[j] && src[j] == j && hi == prefix[j]) atomicAdd(&s_h[j][digit], 1u);
   }
   __syncthreads();
   uint32_t* gh = hist + (size_t)bh * 3 * kRankBins;
   for (int i = threadIdx.x; i < 3 * kRankBins; i += kHistThreads) {
-    const uint32_t v = (&s_h[0][0])[i];
-    if (v) atomicAdd(&gh[i], v);
+    const int j = i / kRankBins;
+    const uint32_t v = s_h[src[j]][i - j * kRankBins];
+    if (active[j] && v) atomicAdd(&gh[i], v);
   }
 }
 
