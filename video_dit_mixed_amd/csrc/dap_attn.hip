@@ -218,19 +218,23 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
   TileMover<D, P::VRC, C::NT, C::DIRECT> vt;
   uint32_t kscale = 0;  // E8M0 key scales of the staged tile (4-bit phase), 4 bytes per thread
 
+  // The current key block and its INT8 scale (8-bit phase) are carried from one iteration to the
+  // next: each iteration loads only the next block's list entry (and scale).
+  const float* ks8 = w.k_i8_scale + (size_t)c.bh * g.Nb;
+  int kb = list_at(c, off);
+  float sk = PH == 1 ? __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(ks8) + kb)) : 0.0f;
+
   // prologue: the first key block's K is loaded
-  {
-    const int kb0 = list_at(c, off);
-    kt.load(k_tile_src<B, D, PH>(g, w, c.bh, kb0), B, c.tid, sK);
-    if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
-      kscale = c.tid < B * (D / 32) / 4
-                   ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb0 * B) * (D / 32) + 4 * c.tid)
-                   : 0x7f7f7f7fu;
-  }
+  kt.load(k_tile_src<B, D, PH>(g, w, c.bh, kb), B, c.tid, sK);
+  if (PH == 2 && c.tid < C::KT * (D / 32) / 4)
+    kscale = c.tid < B * (D / 32) / 4
+                 ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb * B) * (D / 32) + 4 * c.tid)
+                 : 0x7f7f7f7fu;
 
   for (int it = 0; it < np; ++it) {
-    const int kb = list_at(c, off + it);
-    const int kb_next = it + 1 < np ? list_at(c, off + it + 1) : kb;
+    // consumed at the end of this iteration (its latency hides behind the barrier and Q K^T)
+    const int kb_next = list_at(c, off + min(it + 1, np - 1));  // the last block re-reads its own entry
+    const float sk_next = PH == 1 ? __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(ks8) + kb_next)) : 0.0f;
     // real extent of key block kb (regions at the high-y / high-x edge hold padding)
     const int per = g.nby * g.nbx;
     const int rem = kb % per;
@@ -266,7 +270,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     // order and c_scale = 0 gives 0 either way)
     float c_scale = kLog2e * inv_sqrt_d;
     if (PH == 1)
-      c_scale = s_q * __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(w.k_i8_scale) + (size_t)c.bh * g.Nb + kb)) *
+      c_scale = s_q * sk *
                 (kLog2e * inv_sqrt_d);
     f32x16 S[C::MT];  // the 8-bit phase keeps its int32 sums here (bit patterns) until converted
     float mx = -INFINITY;
@@ -436,6 +440,8 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
       psum *= 0.00390625f;  // 2^-8, exact
     }
     l_run = alpha * l_run + psum;
+    kb = kb_next;
+    sk = sk_next;
   }
 }
 
