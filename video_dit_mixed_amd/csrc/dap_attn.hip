@@ -92,6 +92,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// A query's two score lanes are l and l ^ 32.  v_permlane32_swap of a register with itself leaves
+// {x[l], x[l ^ 32]} in the two results of every lane (in an order that depends on the half), so
+// their max / sum is the combined value, with no LDS round trip.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Per-workgroup context of one (head, query block) row.
 struct RowCtx {
   int bh, qb, tid, n, gh;
@@ -351,7 +363,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
       qk_all(std::false_type{});
 
     // ---- online softmax statistics in the log2 domain, one running-max update per key block
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     if (full) mx *= c_scale;
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -515,7 +527,7 @@ void attn_kernel(Geo g, Ws w) {
   if (n4 > 0) run_phase<B, D, 2>(g, w, c, O, m_run, l_run, n4, n16 + n8, sK, sV, sKs, sBias);
 
   // ---- finalise: O / l (0 when no pair was kept), undo the low-bit units, bf16 out
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = halves_sum(l_run);
   const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
   if (c.qok) {
     uint16_t* dst = w.out + c.qrow * D;
