@@ -180,7 +180,10 @@ __device__ __forceinline__ void wait_vm() {
 
 // Workgroup barrier without a memory fence (LDS traffic is ordered by lgkmcnt; global loads that
 // are still in flight belong to the next tile and must not be waited for here).
-__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), visible to the compiler's own wait tracking
+  asm volatile("s_barrier" ::: "memory");
+}
 
 template <int B, int D, int PH>
 __device__ __forceinline__ const uint8_t* k_tile_src(const Geo& g, const Ws& w, int bh, int kb) {
