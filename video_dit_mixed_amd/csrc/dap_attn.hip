@@ -21,9 +21,9 @@
 // Key and V tiles are staged through LDS in an XOR-swizzled layout (bank-conflict-free reads).
 // For 128-token blocks the load unit writes them into LDS directly (buffer loads with an LDS
 // destination), so no registers hold them on the way; smaller blocks stage them through
-// registers.  Two barriers per key block: after the first, the tile's V is issued and lands
-// during Q K^T and the softmax; after the second, the next tile's K is issued and lands during
-// the P V products.  The matrix-core operand orders were fixed when the operands were packed, so
+// registers.  Two barriers per key block: after the first, the tile's V is issued (a quarter
+// after each m-tile's Q K^T products) and lands during Q K^T and the softmax; after the second,
+// the next tile's K is issued and lands during the P V products.  The matrix-core operand orders were fixed when the operands were packed, so
 // every LDS read is one or two 16-byte loads.
 #include <type_traits>
 
@@ -145,11 +145,15 @@ struct TileMover {
   uint4 v[kDirect ? 1 : N];
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ gsrc, int valid, int tid, uint8_t* lds) {
+    load_part<0, N>(gsrc, valid, tid, lds);
+  }
+  template <int J0, int J1>
+  __device__ __forceinline__ void load_part(const uint8_t* __restrict__ gsrc, int valid, int tid, uint8_t* lds) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(gsrc), (short)0, valid * RC * 16, kRsrcWord3);
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const int sl = tid + j * NT;
       const int r = sl / RC, pc = sl - (sl / RC) * RC;
       const int off = r * (RC * 16) + 16 * swz<RC>(r, pc);
@@ -268,8 +272,19 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     }
     if constexpr (C::DIRECT) wait_vm<0>();  // K (issued one key block earlier) has landed
     bar();  // K, scales and bias visible; every wave is done with the previous P V
-    // this tile's V streams in while Q K^T and the softmax run
-    if constexpr (C::DIRECT) vt.load(v_tile_src<B, D, PH>(g, w, c.bh, kb), D, c.tid, sV);
+    // This tile's V streams in while Q K^T and the softmax run; its loads are issued a quarter after
+    // each m-tile's products, so the first products do not wait behind the whole tile's issue.
+    constexpr int NVL = TileMover<D, P::VRC, C::NT, C::DIRECT>::N;
+    static_assert(!C::DIRECT || C::MT == 4, "direct loads: 128-token blocks");  // quarters may be empty
+    const uint8_t* vsrc = v_tile_src<B, D, PH>(g, w, c.bh, kb);
+    auto v_part = [&](int mt) {  // mt is a constant in the unrolled loop below
+      if constexpr (C::DIRECT) {
+        if (mt == 0) vt.template load_part<0, NVL / 4>(vsrc, D, c.tid, sV);
+        if (mt == 1) vt.template load_part<NVL / 4, NVL / 2>(vsrc, D, c.tid, sV);
+        if (mt == 2) vt.template load_part<NVL / 2, 3 * NVL / 4>(vsrc, D, c.tid, sV);
+        if (mt == 3) vt.template load_part<3 * NVL / 4, NVL>(vsrc, D, c.tid, sV);
+      }
+    };
     // per-lane LDS addresses are recomputed in every iteration (a few integer ops) instead of
     // being hoisted out of the loop, where they would pin dozens of registers
     int ln = lane;
@@ -349,9 +364,11 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     // conversion and maximum, which then run while the matrix core works
     auto qk_all = [&](auto full_c) {
       qk_tile(0);
+      v_part(0);
 #pragma unroll
       for (int mt = 1; mt < C::MT; ++mt) {
         qk_tile(mt);
+        v_part(mt);
         qk_post(mt - 1, full_c);
       }
       qk_post(C::MT - 1, full_c);
