@@ -286,6 +286,28 @@ def test_all_draft_scores_tied(quota):
     _run_case(w, inputs=(Q, K, V))
 
 
+@pytest.mark.parametrize("geom", [(4, 40, 64, 128, 8, 16), (4, 24, 40, 64, 8, 8)])
+def test_zero_blocks_and_channels(geom):
+    # Exact zeros where a scale becomes 0: two V channels of head 0 (FP8 scale 0, so the
+    # accumulator's unit change multiplies those channels by 0), one key region of head 0 (INT8 block
+    # scale 0, E8M0 code 0, pooled descriptor 0) and one query region of head 1.  Every precision
+    # is used; 128-token blocks load tiles straight into LDS, 64-token blocks through registers.
+    T, H, W, D, rh, rw = geom
+    w = synth.Workload("zeros", T, H, W, 2, D, rh, rw, 0.5, (4000, 2000, 2000, 2000), seed=4245)
+    Q, K, V = synth.make_inputs(w)
+    V[0, 0, :, 3] = 0
+    V[0, 0, :, D - 5] = 0
+
+    def region_tokens(t, ry, rx):
+        ys, xs = np.meshgrid(np.arange(ry * rh, (ry + 1) * rh), np.arange(rx * rw, (rx + 1) * rw),
+                             indexing="ij")
+        return ((t * H + ys) * W + xs).ravel()
+
+    K[0, 0, region_tokens(0, 1, 2), :] = 0
+    Q[0, 1, region_tokens(1, 2, 1), :] = 0
+    _run_case(w, inputs=(Q, K, V))
+
+
 # ------------------------------------------------------------------------------------ full size
 
 @pytest.mark.parametrize("wi", [2, 3, 4])
