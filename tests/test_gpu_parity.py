@@ -308,6 +308,13 @@ def test_zero_blocks_and_channels(geom):
     _run_case(w, inputs=(Q, K, V))
 
 
+def test_max_regions():
+    # The largest supported map: 4096 regions per head (one 8x16 region per frame), so pair
+    # indices use all 24 bits and list entries reach 4095; sampled query blocks.
+    w = synth.Workload("maxnb", 4096, 8, 16, 1, 64, 8, 16, 0.5, (5000, 1500, 1500, 2000), seed=4246)
+    _run_case(w, exact_heads=[0], sample_blocks=8, check_heads=[0])
+
+
 # ------------------------------------------------------------------------------------ full size
 
 @pytest.mark.parametrize("wi", [2, 3, 4])
