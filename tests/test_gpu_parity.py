@@ -308,6 +308,15 @@ def test_zero_blocks_and_channels(geom):
     _run_case(w, inputs=(Q, K, V))
 
 
+@pytest.mark.parametrize("geom", [(4, 40, 64, 128, 8, 16), (4, 24, 40, 64, 8, 8)])
+def test_very_sparse(geom):
+    # 0.1 % of the pairs kept (16-bit and 8-bit): most query blocks have no kept pair and must
+    # output 0, the others attend to one or two key blocks.
+    T, H, W, D, rh, rw = geom
+    w = synth.Workload("sparse", T, H, W, 2, D, rh, rw, 0.5, (9990, 0, 5, 5), seed=4247)
+    _run_case(w)
+
+
 def test_max_regions():
     # The largest supported map: 4096 regions per head (one 8x16 region per frame), so pair
     # indices use all 24 bits and list entries reach 4095; sampled query blocks.
