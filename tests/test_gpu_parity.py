@@ -254,6 +254,58 @@ def test_deterministic_bitwise():
         assert torch.equal(b.section(ws1, L, name, dt, shape), b.section(ws2, L, name, dt, shape))
 
 
+def test_workspace_contents_do_not_leak_between_layers():
+    """The workspace is caller-owned scratch: whatever it holds before a layer (all-ones bytes, or
+    the lists, counters, maps and operands of a previous layer with other inputs and quotas) must not
+    change a single output bit, block-map entry or draft score."""
+    import torch
+    w = synth.workload(1).with_(heads=3)
+    w_prev = w.with_(seed=w.seed + 1, quota_bp=(1000, 3000, 3000, 3000))
+    cfg, cfg_prev = b.Config.from_workload(w), b.Config.from_workload(w_prev)
+    q, k, v = to_device(*synth.make_inputs(w))
+    qp, kp, vp = to_device(*synth.make_inputs(w_prev))
+    nbytes = max(b.workspace_bytes(cfg), b.workspace_bytes(cfg_prev))
+    L = b.workspace_layout(cfg)
+    secs = (("map", torch.uint8, (L["bh"], L["Nb"], L["Nb"])),
+            ("scores", torch.float64, (L["bh"], L["Nb"], L["Nb"])))
+    results = []
+    for before in ("zeros", "ones", "previous layer"):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+        if before == "ones":
+            ws.fill_(0xFF)
+        elif before == "previous layer":
+            b.forward(cfg_prev, qp, kp, vp, ws=ws)
+        log(f"workspace before the layer: {before}")
+        out, _ = b.forward(cfg, q, k, v, ws=ws)
+        torch.cuda.synchronize()
+        results.append((out, [b.section(ws, L, n, dt, s).clone() for n, dt, s in secs]))
+    for out, sec in results[1:]:
+        assert torch.equal(out, results[0][0])
+        for a, r in zip(sec, results[0][1]):
+            assert torch.equal(a, r)
+
+
+def test_calls_follow_the_callers_stream():
+    """Every call is ordered on the stream it is handed: the inputs are produced on a side stream
+    behind a long spin, and the whole layer is enqueued on that stream with no host wait in between;
+    the result must equal the default-stream run bit for bit."""
+    import torch
+    w = synth.workload(1).with_(heads=3)
+    cfg = b.Config.from_workload(w)
+    q, k, v = to_device(*synth.make_inputs(w))
+    _, ref_out, _ = run_gpu(cfg, q, k, v)
+    ws = torch.full((b.workspace_bytes(cfg),), 0xFF, dtype=torch.uint8, device=q.device)
+    out = torch.full_like(q, float("nan"))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(50_000_000)  # a bounded spin of about 20 ms on the side stream
+        q2, k2, v2 = q.clone(), k.clone(), v.clone()
+        b.forward(cfg, q2, k2, v2, ws=ws, out=out, stream=s.cuda_stream)
+    s.synchronize()
+    assert torch.equal(out, ref_out)
+
+
 # ------------------------------------------------------------------------------------ 128-token blocks
 # 128-token blocks (the full-size configurations) at CPU-checkable sizes.
 # 20 x 36 latent with 8 x 16 regions: the last region row holds 4 real rows (keys 64..127 of its
