@@ -257,12 +257,23 @@ __global__ __launch_bounds__(kThreads) void v_amax_kernel(Geo g, const uint16_t*
   float m[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) m[j] = 0.0f;
-  for (int n = n0 + r0; n < n1; n += RP) {
+  auto fold = [&](const uint4& u) {
     float x[8];
-    unpack8(*reinterpret_cast<const uint4*>(src + (size_t)n * D + c * 8), x);
+    unpack8(u, x);
 #pragma unroll
     for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(x[j]));
+  };
+  // eight rows per round: their loads are all in flight before the first maximum
+  constexpr int U = 8;
+  int n = n0 + r0;
+  for (; n + (U - 1) * RP < n1; n += U * RP) {
+    uint4 u[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) u[i] = *reinterpret_cast<const uint4*>(src + (size_t)(n + i * RP) * D + c * 8);
+#pragma unroll
+    for (int i = 0; i < U; ++i) fold(u[i]);
   }
+  for (; n < n1; n += RP) fold(*reinterpret_cast<const uint4*>(src + (size_t)n * D + c * 8));
 #pragma unroll
   for (int j = 0; j < 8; ++j) s_max[r0][c * 8 + j] = m[j];
   __syncthreads();
@@ -319,20 +330,31 @@ __global__ __launch_bounds__(kThreads) void v_pack_kernel(Geo g, const uint16_t*
     s_r[tid] = a > 0.0f ? 448.0f / a : 0.0f;
     if (b == 0) w.v_scale[(size_t)bh * D + tid] = a > 0.0f ? a / 448.0f : 0.0f;
   }
-  // gather: key r of the block is region pixel (iy, ix) = (r / rw, r % rw); pad keys are 0
-  for (int i = tid; i < B * CH; i += kThreads) {
-    const int r = i / CH, c = i - (i / CH) * CH;
+  // gather: key r of the block is region pixel (iy, ix) = (r / rw, r % rw); pad keys are 0.
+  // Every load of the thread is issued before the first LDS store.
+  constexpr int MAXI = 128 * CH / kThreads;  // rounds for the largest block
+  uint4 raw[MAXI];
+#pragma unroll
+  for (int p = 0; p < MAXI; ++p) {
+    const int i = tid + p * kThreads;
+    const int r = i / CH, c = i % CH;
     const int iy = r / g.rw, ix = r - (r / g.rw) * g.rw;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (iy < bc.vh && ix < bc.vw) {
+    raw[p] = make_uint4(0, 0, 0, 0);
+    if (i < B * CH && iy < bc.vh && ix < bc.vw) {
       const size_t n = ((size_t)bc.t * g.H + bc.ry * g.rh + iy) * g.W + bc.rx * g.rw + ix;
-      raw = *reinterpret_cast<const uint4*>(src + n * D + c * 8);
+      raw[p] = *reinterpret_cast<const uint4*>(src + n * D + c * 8);
     }
-    uint32_t* dstw = reinterpret_cast<uint32_t*>(s_v + r * PITCH + 16 * c);
-    dstw[0] = raw.x;
-    dstw[1] = raw.y;
-    dstw[2] = raw.z;
-    dstw[3] = raw.w;
+  }
+#pragma unroll
+  for (int p = 0; p < MAXI; ++p) {
+    const int i = tid + p * kThreads;
+    if (i < B * CH) {
+      uint32_t* dstw = reinterpret_cast<uint32_t*>(s_v + (i / CH) * PITCH + 16 * (i % CH));
+      dstw[0] = raw[p].x;
+      dstw[1] = raw[p].y;
+      dstw[2] = raw[p].z;
+      dstw[3] = raw[p].w;
+    }
   }
   __syncthreads();
   auto val = [&](int key, int d) -> uint32_t {
