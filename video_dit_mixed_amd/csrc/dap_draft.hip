@@ -30,7 +30,8 @@ typedef __attribute__((ext_vector_type(4))) double f64x4;
 // pitch of 18 doubles: the 16 rows x 2 channels of a half-wave read land in 32 distinct bank pairs.
 // The products of each MFMA are accumulated in channel order with fused multiply-adds, so every
 // logit equals one fma chain over the channels in ascending order (measured bit for bit against a
-// vector-FMA version of this kernel).  Two waves per SIMD: 179 VGPRs.
+// vector-FMA version of this kernel).  The next 16 channels are fetched into registers while the
+// current ones are multiplied.  Two waves per SIMD: 214 VGPRs.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void draft_logits_kernel(Geo g, Ws w) {
   __shared__ __attribute__((aligned(16))) double sQ[kTile * kPitch];
@@ -52,8 +53,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  for (int d0 = 0; d0 < D; d0 += kKc) {
-    double2 qv[4], kv[4];
+  // the next channels' operands are loaded into registers while the current ones are multiplied
+  double2 qv[4], kv[4];
+  auto fetch = [&](int d0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       qv[e] = qr < g.Nb ? *reinterpret_cast<const double2*>(qbar + (size_t)qr * D + d0 + sc + 2 * e)
@@ -61,6 +63,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       kv[e] = kr < g.Nb ? *reinterpret_cast<const double2*>(kbar + (size_t)kr * D + d0 + sc + 2 * e)
                         : double2{0.0, 0.0};
     }
+  };
+  fetch(0);
+  for (int d0 = 0; d0 < D; d0 += kKc) {
     __syncthreads();  // every wave is done with the previous channels
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -68,6 +73,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       *reinterpret_cast<double2*>(sK + sr * kPitch + sc + 2 * e) = kv[e];
     }
     __syncthreads();
+    if (d0 + kKc < D) fetch(d0 + kKc);
 #pragma unroll
     for (int k4 = 0; k4 < kKc; k4 += 4) {
       double a[4], b[4];
