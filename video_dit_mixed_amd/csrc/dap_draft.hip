@@ -129,13 +129,27 @@ __global__ __launch_bounds__(256) void draft_mix_kernel(Geo g, Ws w) {
   double* ea = s_e;
   double* em = s_e + Nb;
   double ma = -INFINITY, mm = -INFINITY;
-  for (int j = threadIdx.x; j < Nb; j += blockDim.x) {
-    const double a = La[j], m = Lm[j];
+  auto take = [&](int j, double a, double m) {
     ea[j] = a;
     em[j] = m;
     ma = fmax(ma, a);
     mm = fmax(mm, m);
+  };
+  // four rounds of loads in flight per thread (the maxima are exact in any order)
+  constexpr int U = 4;
+  const int nt = blockDim.x;
+  int j = threadIdx.x;
+  for (; j + (U - 1) * nt < Nb; j += U * nt) {
+    double a[U], m[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u] = La[j + u * nt];
+      m[u] = Lm[j + u * nt];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) take(j + u * nt, a[u], m[u]);
   }
+  for (; j < Nb; j += nt) take(j, La[j], Lm[j]);
   ma = block_reduce(ma, true, s_red);
   mm = block_reduce(mm, true, s_red);
   double sa = 0.0, sm = 0.0;
