@@ -154,3 +154,37 @@ def test_binding_checks_tensors_before_the_library_call():
         b.restore(cfg, ws, torch.zeros((1, 1), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="bytes"):
         b.draft_rank(cfg, ws, map_out=torch.zeros(3, dtype=torch.uint8))
+
+
+def _oracle_imports(path):
+    """(enclosing top-level function or None, line) of every import of the oracle package in a file."""
+    import ast
+    tree = ast.parse(open(path).read(), filename=path)
+    found = []
+
+    def visit(node, fn):
+        for child in ast.iter_child_nodes(node):
+            inner = child.name if isinstance(child, (ast.FunctionDef, ast.AsyncFunctionDef)) and fn is None else fn
+            names = []
+            if isinstance(child, ast.Import):
+                names = [a.name for a in child.names]
+            elif isinstance(child, ast.ImportFrom):
+                names = [child.module or ""]
+            if any(n == "oracle" or n.startswith("oracle.") for n in names):
+                found.append((fn, child.lineno))
+            visit(child, inner)
+
+    visit(tree, None)
+    return found
+
+
+def test_product_path_never_reaches_the_oracle():
+    """The oracle is test infrastructure: no module of the package imports it, and bench.py and the
+    entry points reach it only from the CPU-baseline leg and from smoke() (the check against it)."""
+    import glob
+    pkg = glob.glob(os.path.join(ROOT, "video_dit_mixed_amd", "**", "*.py"), recursive=True)
+    assert pkg
+    for p in pkg:
+        assert _oracle_imports(p) == [], p
+    assert {fn for fn, _ in _oracle_imports(os.path.join(ROOT, "bench.py"))} == {"cpu_baseline"}
+    assert {fn for fn, _ in _oracle_imports(os.path.join(ROOT, "__graft_entry__.py"))} <= {"smoke", "build"}
