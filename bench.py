@@ -22,7 +22,8 @@ dap_prepare -> dap_draft_rank -> dap_attention -> dap_restore.  Prints one JSON 
                 HIP events on the launch stream; peak = flops / T_roof with T_roof the time every
                 kept pair would take at the dense peak of its own precisions (bf16 2.5 PF/s;
                 int8 and fp8 5.0 P/s; fp4 10.1 PF/s)
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload, extrapolated to a layer
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload (a process pool over heads,
+                one worker per core), extrapolated to a layer
 """
 from __future__ import annotations
 
@@ -82,35 +83,85 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, Q, K, V, target_s: float = 15.0):
-    """Time the oracle on one head (all pre-attention steps) plus a sample of its query blocks,
-    then extrapolate linearly to the full layer (heads and query blocks carry equal work)."""
-    import oracle
-    from oracle import pipeline as opipe
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline_head(args):
+    """Pool worker: the oracle on one head of the workload -- every step before attention, then
+    attention over query blocks in a seeded random order until `budget_s` has passed.  Returns
+    (head, prepare seconds, attention seconds, blocks done, Nb)."""
+    from oracle import pipeline as opipe
+    from video_dit_mixed_amd import synth
+    w, bh, budget_s, blas_threads = args
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(blas_threads)
     except Exception:  # pragma: no cover
-        cores = 1
+        limit = None
+    q, k, v = synth.make_head(w, bh)
     t0 = time.perf_counter()
-    r = opipe.prepare_head(Q[0, 0], K[0, 0], V[0, 0], T=w.T, H=w.H, W=w.W, rh=w.region_h,
-                           rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp)
+    r = opipe.prepare_head(q, k, v, T=w.T, H=w.H, W=w.W, rh=w.region_h, rw=w.region_w,
+                           lam=w.lam, quota_bp=w.quota_bp)
     t_prep = time.perf_counter() - t0
     Nb = r.g.Nb
-    rng = np.random.default_rng(0)
-    order = rng.permutation(Nb)
+    order = np.random.default_rng([7, bh]).permutation(Nb)
     done = 0
     t1 = time.perf_counter()
-    while done < Nb and (time.perf_counter() - t1) < target_s:
+    while done < Nb and (time.perf_counter() - t1) < budget_s:
         opipe.attend(r, q_blocks=[int(order[done])])
         done += 1
     t_att = time.perf_counter() - t1
-    heads = w.batch * w.heads
-    per_layer_s = heads * (t_prep + t_att * Nb / max(done, 1))
-    return {"value": per_layer_s * 1e3, "unit": "ms/layer", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 of {heads} heads through pack/pool/draft/rank/quantise "
-                      f"({t_prep:.1f} s) and {done} of {Nb} query blocks through attention "
-                      f"({t_att:.1f} s); extrapolated linearly to {heads} heads x {Nb} blocks"}
+    del limit
+    return bh, t_prep, t_att, done, Nb
+
+
+class CpuBaseline:
+    """The CPU oracle timed on this host's cores: a process pool over heads (heads are independent
+    and carry equal work), one worker per core the process may run on (up to the head count),
+    BLAS threads split between the workers.  The pool is forked when the object is made, which
+    must happen before the GPU is touched, so the workers are plain CPU processes."""
+
+    def __init__(self, w, budget_s: float = 12.0):
+        import multiprocessing as mp
+        self.w = w
+        self.budget_s = budget_s
+        self.cores = len(os.sched_getaffinity(0))
+        heads = w.batch * w.heads
+        self.workers = max(1, min(self.cores, heads))
+        self.blas = max(1, self.cores // self.workers)
+        self.pool = mp.get_context("fork").Pool(self.workers)
+
+    def run(self):
+        w = self.w
+        heads = w.batch * w.heads
+        sample = list(range(self.workers))          # one head per worker, all at once
+        t0 = time.perf_counter()
+        res = self.pool.map(_cpu_baseline_head,
+                            [(w, bh, self.budget_s, self.blas) for bh in sample], chunksize=1)
+        wall = time.perf_counter() - t0
+        self.pool.close()
+        self.pool.join()
+        full = [tp + ta * nb / max(done, 1) for _, tp, ta, done, nb in res]
+        rounds = -(-heads // self.workers)
+        per_layer_s = rounds * statistics.mean(full)
+        done = [d for _, _, _, d, _ in res]
+        nb = res[0][4]
+        return {"value": round(per_layer_s * 1e3, 1), "unit": "ms/layer", "cores": self.cores,
+                "kind": "oracle", "cpu_model": _cpu_model(), "workers": self.workers,
+                "blas_threads_per_worker": self.blas, "heads_sampled": len(sample),
+                "sample": f"{len(sample)} of {heads} heads in parallel (one per worker): every "
+                          f"step before attention in full ({statistics.mean([r[1] for r in res]):.1f} s "
+                          f"per head) and {min(done)}-{max(done)} of {nb} query blocks through "
+                          f"attention ({self.budget_s:.0f} s budget); per head extrapolated "
+                          f"linearly to {nb} blocks, per layer x {rounds} rounds of "
+                          f"{self.workers} heads; {wall:.0f} s wall for the sample"}
 
 
 # ------------------------------------------------------------------------------------------ sweep
@@ -367,12 +418,14 @@ def main():
     from video_dit_mixed_amd import binding as b
     from video_dit_mixed_amd import synth
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
     w = synth.workload(args.workload)
     if args.quota:
         w = w.with_(quota_bp=tuple(int(x) for x in args.quota.split(",")))
+    # the CPU baseline's workers are forked now, before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else CpuBaseline(w)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
     cfg = b.Config.from_workload(w)
     L = b.workspace_layout(cfg)
     t_gen = time.perf_counter()
@@ -457,8 +510,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 1 << 30
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, Q, K, V)
+    if cpu is not None:
+        del Q, K, V
+        res["cpu_baseline"] = cpu.run()
     print(json.dumps(res), flush=True)
 
 

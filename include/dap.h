@@ -12,9 +12,10 @@
  *   dap_draft_rank build the lambda-mixed draft attention map from the pooled descriptors, rank all
  *                  region pairs of each head and assign 16-bit / 8-bit / 4-bit / skip by quota
  *                  -- blog section 方法概览 bullets 1 and 2; paper card AI Summary (shared sort).
- *   dap_attention  one attention kernel with precision phases (16 -> 8 -> 4) sharing the
- *                  online-softmax statistics and the output accumulator -- paper card Abstract;
- *                  blog section 方法概览 bullet 4.
+ *   dap_attention  attention over the kept blocks in precision order 16 -> 8 -> 4, one kernel
+ *                  whose phases update the same running max, running sum and output
+ *                  accumulator of each query row -- paper card Abstract; blog section 方法概览
+ *                  bullet 4.
  *   dap_restore    put the output back in the original token order, dropping padding
  *                  -- pith.science, DraftAttention abstract (reorder, attend, restore).
  *
@@ -36,13 +37,24 @@
  *   different workspaces may run concurrently.  Work is enqueued on `stream` (0 = null stream)
  *   and the calls return without synchronising; buffers must stay alive until the enqueued work
  *   completes.  The four calls must be issued in the order prepare -> draft_rank -> attention ->
- *   restore on one workspace, in stream order.
+ *   restore on one workspace, in stream order.  The workspace carries a stage word (see
+ *   dap_layout.off_stage) that enforces this: dap_prepare sets DAP_STAGE_PREPARED; dap_draft_rank
+ *   moves a prepared (or later) workspace to DAP_STAGE_RANKED; dap_attention runs only on a
+ *   ranked (or attended) workspace and moves it to DAP_STAGE_ATTENDED; dap_restore copies the
+ *   attention output only from an attended workspace.  A call that finds the wrong stage, or a
+ *   stage written under another configuration, still returns DAP_OK (the check runs on the
+ *   device, in stream order), writes zeros instead of its result (attention: the packed output;
+ *   restore: out) and leaves the stage at DAP_STAGE_BROKEN until the next dap_prepare.  The
+ *   caller can read the two stage words after synchronising.  dap_draft_rank on an unprepared
+ *   workspace ranks whatever the pooled sections hold (its map_out / scores_out copies are then
+ *   meaningless) and marks the stage broken.
  *
  * Errors
  *   Host-side validation runs before any HIP call and returns DAP_E_INVALID (null pointer, bad
  *   size, lambda outside [0, 1], negative quota or quota sum above 10000, misaligned pointer),
  *   DAP_E_UNSUPPORTED (head_dim not 64/128, region size not 16/64/128 tokens, more than 4096
- *   regions per head) or DAP_E_WORKSPACE (ws_bytes too small).  A failed kernel launch returns
+ *   regions per head, an fp4_format this build does not provide) or DAP_E_WORKSPACE (ws_bytes
+ *   too small).  A failed kernel launch returns
  *   DAP_E_HIP.  Device faults surface at the caller's next synchronisation.  Non-finite inputs
  *   are outside the contract.
  */
@@ -58,7 +70,19 @@
 extern "C" {
 #endif
 
-#define DAP_ABI_VERSION 1
+#define DAP_ABI_VERSION 2
+
+/* Stage word values (first 32-bit word of the stage section); the second word is a tag of the
+ * configuration that wrote it. */
+#define DAP_STAGE_PREPARED 0xDA900001u
+#define DAP_STAGE_RANKED 0xDA900002u
+#define DAP_STAGE_ATTENDED 0xDA900003u
+#define DAP_STAGE_BROKEN 0xDA9000FFu
+
+/* 4-bit operand formats (dap_config.fp4_format). */
+#define DAP_FP4_MXFP4 0 /* OCP MXFP4: E2M1 codes, one E8M0 power-of-two scale per 32 channels */
+#define DAP_FP4_NVFP4 1 /* E2M1 codes, one E4M3 scale per 16 channels over one fp32 scale per
+                          (head, tensor) */
 
 typedef enum {
   DAP_OK = 0,
@@ -77,6 +101,7 @@ typedef struct {
   int32_t region_w;     /* region columns (width); region_h*region_w in {16, 64, 128} */
   double lambda;        /* draft-map mix weight of the max-pooled map, in [0, 1] */
   int32_t quota_bp[4];  /* skip, 4-bit, 8-bit, 16-bit, basis points */
+  int32_t fp4_format;   /* DAP_FP4_MXFP4 or DAP_FP4_NVFP4 */
 } dap_config;
 
 /* Derived sizes and the byte offsets of every workspace section (all 256-byte aligned).
@@ -100,8 +125,10 @@ typedef struct {
  *   counts          [bh][Nb][4] int32: n16, n8, n4, 0
  *   zeros           256 zero bytes (source of the all-zero key rows a 16-token block pads to)
  *   order           [8][bh * ceil(Nb/8)] uint32 (bh << 16 | qb): attention work order, one slice per
- *                   accelerator die (XCD) -- rows with similar key lists share a slice
- *   out             [bh][Np][D] bf16 attention output in packed order */
+ *                   accelerator die (XCD); each head's rows are ranked by cost and dealt to the
+ *                   dies in snake order
+ *   out             [bh][Np][D] bf16 attention output in packed order
+ *   stage           2 x uint32: stage word (DAP_STAGE_*) and configuration tag */
 typedef struct {
   int32_t Hp, Wp, nby, nbx, Nb, B, Np, kp8, bh, D;
   int64_t pairs, c16, c8, c4;
@@ -112,6 +139,7 @@ typedef struct {
   uint64_t off_q_avg, off_q_max, off_k_avg, off_k_max;
   uint64_t off_scores, off_lmax, off_rank_state, off_rank_hist;
   uint64_t off_map, off_lists, off_counts, off_out, off_zeros, off_order;
+  uint64_t off_stage;
   uint64_t total_bytes;
 } dap_layout;
 

@@ -1,11 +1,10 @@
 """Phased mixed-precision block-sparse attention with shared online-softmax state.
 Oracle: test infrastructure only.
 
-Follows: newx.sg paper card, Abstract (one attention kernel with precision-specific phases that
-share data movement, softmax statistics and output accumulation); pchao.org blog, section 方法概览
-(the overview paragraph and bullet 4: phases share the softmax statistics and the output
-accumulation, and rescale by the quantisation scales at phase boundaries, with no separate
-write-back and merge per precision).
+Follows: newx.sg paper card, Abstract, and pchao.org blog, section 方法概览 (overview paragraph and
+bullet 4): a query row's kept blocks of every precision update one running maximum, one running
+sum and one output accumulator, with the quantisation scales applied where the precision changes,
+instead of one partial result per precision merged afterwards.
 
 Per query block qb, over its real query rows, with running max m = -inf, sum l = 0, output O = 0:
   for phase in (16-bit, 8-bit, 4-bit), for each key block kb of that level in ascending order:

@@ -2,9 +2,9 @@
 Oracle: test infrastructure only.
 
 Follows:
-  * pooling -- newx.sg paper card, Abstract (spatial 2D average- and max-pooled queries and keys);
-    pchao.org blog, section 方法概览 bullet 1 (an average descriptor and a channel-wise max
-    descriptor per region);
+  * pooling -- newx.sg paper card, Abstract (the draft is computed from queries and keys pooled
+    over 2D spatial regions, by mean and by maximum); pchao.org blog, section 方法概览 bullet 1
+    (one mean descriptor and one per-channel maximum descriptor per region);
   * draft maps and mix -- same bullet (an Avg draft map and a Max draft map are formed, then mixed
     with weight lambda; lambda = 0 falls back to average-only guidance as in DraftAttention v1);
     Figure 2 caption (weighted mixture of the pooled draft maps guides block selection);
@@ -90,9 +90,3 @@ def assign_levels(rank: np.ndarray, cuts) -> np.ndarray:
     lv[rank < c16] = LEVEL_16
     return lv
 
-
-def row_lists(levels: np.ndarray):
-    """Per query block and level: key blocks in ascending order.  Returns
-    {LEVEL_16: [arr per qb], LEVEL_8: [...], LEVEL_4: [...]}."""
-    return {lv: [np.flatnonzero(levels[qb] == lv) for qb in range(levels.shape[0])]
-            for lv in (LEVEL_16, LEVEL_8, LEVEL_4)}

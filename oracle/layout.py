@@ -1,9 +1,9 @@
 """Region geometry, pack (reorder + pad) and unpack (restore).  Oracle: test infrastructure only.
 
-Follows: pchao.org blog on DraftAttention2, Figure 3(a) caption (compact spatial regions are packed
-into contiguous token blocks; gray cells are padding) and section 方法概览 bullet 1 (tokens are split
-into spatial regions per frame); pith.science DraftAttention abstract (reorder before attention,
-restore the original order afterwards).
+Follows: pchao.org blog on DraftAttention2, Figure 3(a) caption (each spatial region of a frame
+becomes one run of consecutive rows, with pad cells where the frame does not fill the region) and
+section 方法概览 bullet 1 (the per-frame spatial regions); pith.science DraftAttention abstract
+(the token order is changed before attention and changed back after it).
 
 Readings (the pages are silent on these):
   R1  inputs are [batch, heads, N, D]; token n = (t*H + y)*W + x.

@@ -16,7 +16,10 @@ Readings:
       format the gfx950 scaled matrix cores consume.)
   R20 FP8 V: one fp32 scale per (head, channel) over real tokens; e4m3fn codes, RNE, saturating.
   R26 all-zero blocks / groups / channels: INT8 codes 0 with scale 0; MX exponent -127;
-      FP8 codes 0 with scale 0.
+      FP8 codes 0 with scale 0.  A block or channel whose maximum is so small that the fp32
+      reciprocal of the quantiser (127/a, 448/a) overflows is treated the same way (below about
+      3.7e-37 for INT8, 1.3e-36 for FP8 V): its values are zero for every practical purpose, and
+      an infinite reciprocal would turn its zeros into NaN codes.
 Sign of a code: the IEEE sign bit of the input, also when the magnitude rounds to zero.
 """
 from __future__ import annotations
@@ -118,11 +121,15 @@ def int8_block(x: np.ndarray):
     """Symmetric INT8 of one token block (all rows and channels share one scale).
 
     x: fp64 values of bf16 inputs (pad rows are 0).  Returns (codes int8, scale float32).
-    a = max|x|; r = f32(127/a); code = clamp(rne(f32(x*r)), -127, 127); s = f32(a/127)."""
+    a = max|x|; r = f32(127/a); code = clamp(rne(f32(x*r)), -127, 127); s = f32(a/127).
+    a = 0, or r not finite (a below about 3.7e-37): codes 0, s = 0 (R26)."""
     a = F32(np.max(np.abs(x)))
     if a == 0:
         return np.zeros(x.shape, np.int8), F32(0.0)
-    r = F32(127.0) / a
+    with np.errstate(over="ignore"):
+        r = F32(127.0) / a
+    if not np.isfinite(r):
+        return np.zeros(x.shape, np.int8), F32(0.0)
     c = np.clip(np.rint(np.asarray(x, dtype=F32) * r), -127, 127)
     return c.astype(np.int8), F32(a / F32(127.0))
 
@@ -199,10 +206,13 @@ def fp8_v(v_real: np.ndarray, vp: np.ndarray):
     v_real: [N, D] fp64 values of bf16 V (real tokens) -- defines the scale.
     vp:     [Np, D] packed V (pad rows 0) -- the rows that get codes.
     a_d = max|V[:, d]|; r = f32(448/a_d); codes = e4m3fn_rne_sat(f32(V*r)); s_d = f32(a_d/448).
+    a_d = 0, or r not finite (a_d below about 1.3e-36): codes 0, s_d = 0 (R26).
     Returns (codes uint8 [Np, D], scale float32 [D])."""
     a = np.max(np.abs(v_real), axis=0).astype(F32)
-    zero = a == 0
-    r = np.where(zero, F32(0), F32(448.0) / np.where(zero, F32(1), a)).astype(F32)
+    with np.errstate(over="ignore"):
+        r_raw = (F32(448.0) / np.where(a == 0, F32(1), a)).astype(F32)
+    zero = (a == 0) | ~np.isfinite(r_raw)
+    r = np.where(zero, F32(0), r_raw).astype(F32)
     y = (np.asarray(vp, dtype=F32) * r[None, :]).astype(F32)
     vals = e4m3fn_rne_sat(y.astype(np.float64))
     codes = e4m3fn_encode(vals, np.signbit(vp))

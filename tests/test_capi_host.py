@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert b.abi_version() == 1
+    assert b.abi_version() == 2
     assert b.status_string(0) == "ok"
     assert "workspace" in b.status_string(3)
 
@@ -57,6 +57,8 @@ def _cfg(**kw):
     (dict(T=1, H=2**31 - 1, W=16, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),
     (dict(T=2**31 - 1, H=2**31 - 1, W=2**31 - 1, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),
     (dict(T=4097, H=8, W=16, region_h=8, region_w=16), b.DAP_E_UNSUPPORTED),
+    (dict(fp4_format=2), b.DAP_E_INVALID),
+    (dict(fp4_format=-1), b.DAP_E_INVALID),
 ])
 def test_validation_rejects(kw, status):
     with pytest.raises(b.DapError) as e:
@@ -100,7 +102,7 @@ def _layout_py(w):
              ("k_max", bh * Nb * D * 8), ("scores", bh * Nb * Nb * 8), ("lmax", bh * Nb * Nb * 8),
              ("rank_state", bh * 3 * 32), ("rank_hist", bh * 3 * 2048 * 4), ("map", bh * Nb * Nb),
              ("lists", bh * Nb * Nb * 2), ("counts", bh * Nb * 16), ("out", bh * Np * D * 2),
-             ("zeros", 256), ("order", 8 * bh * -(-Nb // 8) * 4)]
+             ("zeros", 256), ("order", 8 * bh * -(-Nb // 8) * 4), ("stage", 8)]
     off, o = {}, 0
     for name, n in sizes:
         off["off_" + name] = o
@@ -186,5 +188,5 @@ def test_product_path_never_reaches_the_oracle():
     assert pkg
     for p in pkg:
         assert _oracle_imports(p) == [], p
-    assert {fn for fn, _ in _oracle_imports(os.path.join(ROOT, "bench.py"))} == {"cpu_baseline"}
+    assert {fn for fn, _ in _oracle_imports(os.path.join(ROOT, "bench.py"))} == {"_cpu_baseline_head"}
     assert {fn for fn, _ in _oracle_imports(os.path.join(ROOT, "__graft_entry__.py"))} <= {"smoke", "build"}

@@ -96,10 +96,15 @@ def _check_map(S: Sections, r, L):
         np.testing.assert_array_equal(lst[n16 + n8:n16 + n8 + n4], np.flatnonzero(row == 1))
 
 
-def _check_out(S: Sections, r, blocks):
-    opipe.attend(r, q_blocks=blocks)
+def _check_out(S: Sections, r, blocks, precomputed=None):
+    """Outputs of `blocks` against the oracle; `precomputed` = (rows, fp64 outputs) from the
+    oracle worker pool, else the oracle runs here."""
     B = r.B
     rows = np.concatenate([qb * B + np.flatnonzero(r.valid[qb]) for qb in blocks])
+    if precomputed is None:
+        opipe.attend(r, q_blocks=blocks)
+    else:
+        r.out_packed[precomputed[0]] = precomputed[1]
     ref = r.out_packed[rows]
     from oracle import quant
     ref = quant.bf16_rne(ref)
@@ -136,7 +141,15 @@ def _sample_blocks(r, S, k=12, seed=0):
     return sorted(pick)
 
 
-def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None, inputs=None):
+def _geo_kw(w):
+    return dict(T=w.T, H=w.H, W=w.W, rh=w.region_h, rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp)
+
+
+def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None, inputs=None,
+              all_blocks_heads=()):
+    """`sample_blocks`: compare that many sampled query blocks per checked head (None: all);
+    heads in `all_blocks_heads` are compared over every query block, with the oracle's attention
+    split over the worker pool."""
     log(f"case {w.name} quota={w.quota_bp} lam={w.lam} batch={w.batch}")
     Q, K, V = _inputs(w, exact_heads) if inputs is None else inputs
     cfg = b.Config.from_workload(w)
@@ -151,8 +164,18 @@ def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None, inputs=
         S = Sections(ws, L, bhi)
         _check_prep(S, r, L)
         _check_map(S, r, L)
-        blocks = list(range(r.g.Nb)) if sample_blocks is None else _sample_blocks(r, S, sample_blocks, bhi)
-        _check_out(S, r, blocks)
+        pre = None
+        if sample_blocks is None or bhi in all_blocks_heads:
+            blocks = list(range(r.g.Nb))
+            if bhi in all_blocks_heads:
+                import oracle_pool
+                bb, h = divmod(bhi, w.heads)
+                log(f"head {bhi}: oracle attention over all {r.g.Nb} query blocks "
+                    f"({'pool' if oracle_pool.get() else 'this process'})")
+                pre = oracle_pool.attend_head(Q[bb, h], K[bb, h], V[bb, h], _geo_kw(w), blocks)
+        else:
+            blocks = _sample_blocks(r, S, sample_blocks, bhi)
+        _check_out(S, r, blocks, pre)
         packed.append((bhi, S.out_packed))
     _check_restore(out, packed, L, w)
     _check_order(ws, L)
@@ -306,6 +329,20 @@ def test_calls_follow_the_callers_stream():
     assert torch.equal(out, ref_out)
 
 
+# ------------------------------------------------------------------------------------ 16-token blocks
+# 3 x 13 x 21 latent: every region shape leaves padding on both axes (4x4: 16 x 24 padded grid,
+# 2x8: 14 x 24, 1x16: 13 x 32); one wave per query block, head_dim 64 and 128.
+
+@pytest.mark.parametrize("quota", [(0, 0, 0, 10000), (0, 0, 10000, 0), (0, 10000, 0, 0),
+                                   (2000, 2000, 3000, 3000)])
+@pytest.mark.parametrize("region", [(4, 4), (2, 8), (1, 16)])
+@pytest.mark.parametrize("D", [128, 64])
+def test_block16(D, region, quota):
+    rh, rw = region
+    w = synth.Workload("b16", 3, 13, 21, 2, D, rh, rw, 0.5, quota, seed=4249)
+    _run_case(w)
+
+
 # ------------------------------------------------------------------------------------ 128-token blocks
 # 128-token blocks (the full-size configurations) at CPU-checkable sizes.
 # 20 x 36 latent with 8 x 16 regions: the last region row holds 4 real rows (keys 64..127 of its
@@ -360,6 +397,37 @@ def test_zero_blocks_and_channels(geom):
     _run_case(w, inputs=(Q, K, V))
 
 
+def _scaled_bits(bits, k):
+    """bf16 bits of the values times 2^-k (rounded to bf16; tiny results may be subnormal)."""
+    f = synth.bf16_bits_to_f32(bits).astype(np.float64) * 2.0 ** -k
+    return synth.f32_to_bf16_bits(f.astype(np.float32))
+
+
+@pytest.mark.parametrize("geom", [(4, 40, 64, 128, 8, 16), (4, 24, 40, 64, 8, 8)])
+def test_vanishing_blocks_and_channels(geom):
+    # Values so small that a quantiser's fp32 reciprocal (127/a, 448/a) overflows: such a block or
+    # channel quantises to zero.  Head 0: one key region near 2^-123 (INT8 reciprocal overflows)
+    # and three V channels near 2^-116 (FP8 reciprocal finite, but the reciprocal of its scale
+    # is not: the accumulator's unit change must not overflow), 2^-119 (at the bound) and 2^-122
+    # (reciprocal overflows).  Head 1: one query region near 2^-114 (INT8 scale tiny but nonzero).
+    T, H, W, D, rh, rw = geom
+    w = synth.Workload("vanish", T, H, W, 2, D, rh, rw, 0.5, (4000, 2000, 2000, 2000), seed=4248)
+    Q, K, V = synth.make_inputs(w)
+
+    def region_tokens(t, ry, rx):
+        ys, xs = np.meshgrid(np.arange(ry * rh, (ry + 1) * rh), np.arange(rx * rw, (rx + 1) * rw),
+                             indexing="ij")
+        return ((t * H + ys) * W + xs).ravel()
+
+    kt = region_tokens(0, 1, 2)
+    K[0, 0, kt, :] = _scaled_bits(K[0, 0, kt, :], 128)
+    qt = region_tokens(1, 2, 1)
+    Q[0, 1, qt, :] = _scaled_bits(Q[0, 1, qt, :], 119)
+    for d, k in ((3, 118), (7, 121), (D - 5, 124)):
+        V[0, 0, :, d] = _scaled_bits(V[0, 0, :, d], k)
+    _run_case(w, inputs=(Q, K, V))
+
+
 @pytest.mark.parametrize("geom", [(4, 40, 64, 128, 8, 16), (4, 24, 40, 64, 8, 8)])
 def test_very_sparse(geom):
     # 0.1 % of the pairs kept (16-bit and 8-bit): most query blocks have no kept pair and must
@@ -382,3 +450,11 @@ def test_max_regions():
 def test_parity_full_size(wi):
     w = synth.workload(wi)
     _run_case(w, exact_heads=[0, w.heads - 1], sample_blocks=10, check_heads=[0, w.heads - 1])
+
+
+@pytest.mark.oracle_pool
+def test_parity_full_size_one_head_every_block():
+    # the 720p layer (85/0/7.5/7.5): head 0 over all 990 query blocks, the last head sampled
+    w = synth.workload(2)
+    _run_case(w, exact_heads=[0, w.heads - 1], sample_blocks=10, check_heads=[0, w.heads - 1],
+              all_blocks_heads=(0,))

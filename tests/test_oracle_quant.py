@@ -170,6 +170,33 @@ def test_int8_error_bound_and_absmax_code():
     assert s0 == 0 and not c0.any()
 
 
+# fp32 overflow bound of a correctly rounded quotient: values at or above (2 - 2^-24) * 2^127 round to
+# infinity (IEEE 754 round-to-nearest: the midpoint between the largest finite value and 2^128)
+_F32_OVERFLOW = (2 - Fraction(1, 2 ** 24)) * 2 ** 127
+
+
+def _tiny_bf16_values():
+    """Positive bf16 values from the subnormal range up to 1e-30, every one of them."""
+    f = _all_finite_bf16()
+    return f[(f > 0) & (f < 1e-30)]
+
+
+def test_int8_block_reciprocal_overflow_is_a_zero_block():
+    # Exact rational arithmetic decides for every tiny bf16 maximum whether f32(127/a) overflows;
+    # exactly those blocks must come out as zeros with scale 0, all others with the +-127 code.
+    hits = 0
+    for a in _tiny_bf16_values():
+        overflow = Fraction(127) / Fraction(float(a)) >= _F32_OVERFLOW
+        x = np.array([[a, -a / 2, 0.0, a / 4]])
+        codes, s = quant.int8_block(x)
+        if overflow:
+            hits += 1
+            assert s == 0 and not codes.any(), a
+        else:
+            assert codes[0, 0] == 127 and codes[0, 2] == 0 and s > 0, a
+    assert 0 < hits < _tiny_bf16_values().size
+
+
 # ---------------------------------------------------------------------------------------- FP8 V
 
 def test_fp8_v_channel_scale_and_zero_channel():
@@ -187,6 +214,24 @@ def test_fp8_v_channel_scale_and_zero_channel():
     big = np.abs(vp) > np.max(np.abs(v), axis=0) * 2.0 ** -6
     assert np.all(np.abs(deq - vp)[big] <= np.abs(vp)[big] * 2.0 ** -4 * 1.0001)
     assert not codes[100:].any()
+
+
+def test_fp8_v_reciprocal_overflow_is_a_zero_channel():
+    # one channel per tiny bf16 maximum; a channel is zero (codes 0, scale 0) exactly when the exact
+    # quotient 448/a rounds to fp32 infinity, otherwise its maximum gets the code for +-448
+    tiny = _tiny_bf16_values()
+    v = np.zeros((3, tiny.size))
+    v[0] = tiny
+    v[1] = -tiny / 2
+    vp = np.concatenate([v, np.zeros((2, tiny.size))])
+    codes, s = quant.fp8_v(v, vp)
+    over = np.array([Fraction(448) / Fraction(float(a)) >= _F32_OVERFLOW for a in tiny])
+    assert 0 < over.sum() < tiny.size
+    assert np.all(s[over] == 0) and not codes[:, over].any()
+    ok = ~over
+    assert np.all(s[ok] > 0)
+    assert np.all(quant.e4m3fn_decode(codes[0, ok]) == 448.0)
+    assert np.all(np.isfinite(quant.e4m3fn_decode(codes[:, ok])))
 
 
 def test_nvfp4_matches_brute_force_nearest_grid_point():

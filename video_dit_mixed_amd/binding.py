@@ -18,6 +18,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdap.so")
 
 DAP_OK, DAP_E_INVALID, DAP_E_UNSUPPORTED, DAP_E_WORKSPACE, DAP_E_HIP = range(5)
+ABI_VERSION = 2
+STAGE_PREPARED, STAGE_RANKED, STAGE_ATTENDED, STAGE_BROKEN = (0xDA900001, 0xDA900002, 0xDA900003,
+                                                              0xDA9000FF)
+FP4_MXFP4, FP4_NVFP4 = 0, 1
 LEVEL_SKIP, LEVEL_4, LEVEL_8, LEVEL_16 = 0, 1, 2, 3
 EXPORTED = ("dap_abi_version", "dap_workspace_bytes", "dap_workspace_layout", "dap_prepare",
             "dap_draft_rank", "dap_attention", "dap_restore", "dap_status_string")
@@ -33,7 +37,8 @@ class _Config(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("region_h", ctypes.c_int32), ("region_w", ctypes.c_int32),
-                ("lam", ctypes.c_double), ("quota_bp", ctypes.c_int32 * 4)]
+                ("lam", ctypes.c_double), ("quota_bp", ctypes.c_int32 * 4),
+                ("fp4_format", ctypes.c_int32)]
 
 
 _LAYOUT_INT32 = ["Hp", "Wp", "nby", "nbx", "Nb", "B", "Np", "kp8", "bh", "D"]
@@ -41,7 +46,7 @@ _LAYOUT_INT64 = ["pairs", "c16", "c8", "c4"]
 _LAYOUT_OFFS = ["q_bf16", "k_bf16", "vt_bf16", "q_i8", "k_i8", "q_i8_scale", "k_i8_scale",
                 "q_fp4", "k_fp4", "q_e8m0", "k_e8m0", "vt_fp8", "v_scale", "v_amax",
                 "q_avg", "q_max", "k_avg", "k_max", "scores", "lmax", "rank_state", "rank_hist",
-                "map", "lists", "counts", "out", "zeros", "order"]
+                "map", "lists", "counts", "out", "zeros", "order", "stage"]
 
 
 class _Layout(ctypes.Structure):
@@ -63,6 +68,7 @@ class Config:
     region_w: int
     lam: float
     quota_bp: Tuple[int, int, int, int]   # skip, 4-bit, 8-bit, 16-bit (basis points)
+    fp4_format: int = FP4_MXFP4
 
     @classmethod
     def from_workload(cls, w, **override) -> "Config":
@@ -83,6 +89,7 @@ class Config:
         c.lam = float(self.lam)
         for i, q in enumerate(self.quota_bp):
             c.quota_bp[i] = int(q)
+        c.fp4_format = int(self.fp4_format)
         return c
 
 
@@ -115,6 +122,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dap_restore.argtypes = [P(_Config), vp, ctypes.c_size_t, vp, vp]
     lib.dap_status_string.restype = ctypes.c_char_p
     lib.dap_status_string.argtypes = [ctypes.c_int]
+    if lib.dap_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path}: ABI version {lib.dap_abi_version()}, this binding speaks "
+                           f"{ABI_VERSION}: rebuild with `python -m video_dit_mixed_amd.build`")
     _lib = lib
     return lib
 
@@ -249,6 +259,13 @@ def forward(cfg: Config, q, k, v, ws=None, out=None, stream=None):
     attention(cfg, ws, stream)
     restore(cfg, ws, out, stream)
     return out, ws
+
+
+def stage_words(ws, layout: dict):
+    """(stage word, configuration tag) of a workspace, read back to the host (synchronises)."""
+    import torch
+    st = section(ws, layout, "stage", torch.int32, (2,)).cpu().numpy().view("uint32")
+    return int(st[0]), int(st[1])
 
 
 def section(ws, layout: dict, name: str, dtype, shape):

@@ -21,7 +21,7 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdap.so")
 
 SOURCES = ["dap_capi.hip", "dap_prep.hip", "dap_draft.hip", "dap_rank.hip", "dap_attn.hip",
-           "dap_restore.hip"]
+           "dap_restore.hip", "dap_stage.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -1,10 +1,10 @@
 // Mixed-precision block-sparse attention with precision phases (gfx950 matrix cores).
 //
-// Method: "DraftAttention2" -- newx.sg paper card, Abstract (one attention kernel with
-// precision-specific phases sharing data movement, softmax statistics and output accumulation);
-// pchao.org blog, section 方法概览 bullet 4 (phases share the softmax statistics and the output
-// accumulation and rescale by the quantisation scales at phase boundaries; no per-precision
-// write-back and merge) and bullet 2 (16-bit, INT8 and 4-bit blocks).
+// Method: "DraftAttention2" -- newx.sg paper card, Abstract, and pchao.org blog, section 方法概览
+// bullet 4: the kept blocks of all precisions are handled by a single kernel that keeps one set of
+// running softmax statistics and one output accumulator per query row, converts between the
+// precisions' scales where the phase changes and writes the output once; bullet 2 gives the
+// precisions (16-bit, INT8, 4-bit).
 //
 // One workgroup per (head, query block); wave w owns queries 32w..32w+31 of the block.  For every
 // kept key block, in phase order 16 -> 8 -> 4 and ascending kb inside a phase:
@@ -111,6 +111,7 @@ struct RowCtx {
   size_t qrow;            // packed row of this lane's query
   const uint32_t* lists;  // all key-block lists, as 32-bit words
   size_t lbase;           // index of this row's first list entry
+  int nb_last;            // Nb - 1: list entries are clamped to it
 };
 
 // Entry i of the row's key-block list.  The list holds 16-bit entries; the 32-bit word holding
@@ -125,7 +126,9 @@ __device__ __forceinline__ uint32_t uniform_load(const uint32_t* p) {
 __device__ __forceinline__ int list_at(const RowCtx& c, int i) {
   const size_t e = c.lbase + (size_t)i;
   const uint32_t wv = uniform_load(c.lists + (e >> 1));
-  return (int)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+  // an entry beyond the last key block can only come from a workspace the ranking did not write
+  // for this configuration; clamping keeps every tile load inside the workspace
+  return min((int)((e & 1) ? (wv >> 16) : (wv & 0xffffu)), c.nb_last);
 }
 
 // Moves one key block's operand tile from global memory into LDS.  Slot s (16 bytes) of a tile of
@@ -490,12 +493,23 @@ void attn_kernel(Geo g, Ws w) {
   // takes entry j of that die's slice of the work order.
   RowCtx c;
   const int Nb = g.Nb;
+  if (!stage_ok(uniform_load(w.stage), uniform_load(w.stage + 1), g.tag,
+                stage_bit(DAP_STAGE_RANKED) | stage_bit(DAP_STAGE_ATTENDED))) {
+    // the ranking has not run on this workspace for this configuration: the order, counts and
+    // lists are not to be trusted, so workgroup i writes zeros over row i of the packed output
+    const long long i = blockIdx.x;
+    if (i >= (long long)g.bh * Nb) return;
+    uint4* dst = reinterpret_cast<uint4*>(w.out + (size_t)i * B * D);  // row i = bh * Nb + qb
+    for (int t = threadIdx.x; t < B * D / 8; t += C::NT) dst[t] = make_uint4(0, 0, 0, 0);
+    return;
+  }
   {
     const int x = blockIdx.x & (kXcds - 1), j = blockIdx.x / kXcds;
     if (j >= g.bh * xcd_chunk_size(x, Nb)) return;
     const uint32_t item = w.order[(size_t)x * xcd_stride(g.bh, Nb) + j];
     c.bh = __builtin_amdgcn_readfirstlane((int)(item >> 16));
     c.qb = __builtin_amdgcn_readfirstlane((int)(item & 0xffff));
+    if (c.bh >= g.bh || c.qb >= Nb) return;  // cannot happen for an order the ranking wrote
   }
   c.tid = threadIdx.x;
   const int wv = c.tid >> 6, lane = c.tid & 63;
@@ -506,11 +520,13 @@ void attn_kernel(Geo g, Ws w) {
   c.qrow = (size_t)c.bh * g.Np + (size_t)c.qb * B + qr;
   c.lists = reinterpret_cast<const uint32_t*>(w.lists);
   c.lbase = (size_t)c.bh * g.pairs + (size_t)c.qb * Nb;
+  c.nb_last = Nb - 1;
 
   const int32_t* cnt = w.counts + ((size_t)c.bh * Nb + c.qb) * 4;
-  const int n16 = (int)uniform_load(reinterpret_cast<const uint32_t*>(cnt));
-  const int n8 = (int)uniform_load(reinterpret_cast<const uint32_t*>(cnt) + 1);
-  const int n4 = (int)uniform_load(reinterpret_cast<const uint32_t*>(cnt) + 2);
+  // counts clamped so that no list is walked past its row (a no-op for counts the ranking wrote)
+  const int n16 = min(max((int)uniform_load(reinterpret_cast<const uint32_t*>(cnt)), 0), Nb);
+  const int n8 = min(max((int)uniform_load(reinterpret_cast<const uint32_t*>(cnt) + 1), 0), Nb - n16);
+  const int n4 = min(max((int)uniform_load(reinterpret_cast<const uint32_t*>(cnt) + 2), 0), Nb - n16 - n8);
 
   f32x16 O[C::DT];
 #pragma unroll
@@ -540,7 +556,9 @@ void attn_kernel(Geo g, Ws w) {
       for (int r4 = 0; r4 < 4; ++r4) {
         const float s4[4] = {sv[dt][r4].x, sv[dt][r4].y, sv[dt][r4].z, sv[dt][r4].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[dt][4 * r4 + e] *= s4[e] > 0.0f ? 256.0f / s4[e] : 0.0f;
+        // (O 2^8) / s rather than O (2^8 / s): the quotient stays finite for the tiniest
+        // nonzero scales, whose reciprocal would overflow
+        for (int e = 0; e < 4; ++e) O[dt][4 * r4 + e] = s4[e] > 0.0f ? (O[dt][4 * r4 + e] * 256.0f) / s4[e] : 0.0f;
       }
   }
   if (n8 > 0) run_phase<B, D, 1>(g, w, c, O, m_run, l_run, n8, n16, sK, sV, sKs, sBias);

@@ -25,6 +25,8 @@ dap_status validate(const dap_config* c) {
     qsum += c->quota_bp[i];
   }
   if (qsum > 10000) return DAP_E_INVALID;
+  if (c->fp4_format != DAP_FP4_MXFP4 && c->fp4_format != DAP_FP4_NVFP4) return DAP_E_INVALID;
+  if (c->fp4_format != DAP_FP4_MXFP4) return DAP_E_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return DAP_E_UNSUPPORTED;
   const long long B = (long long)c->region_h * c->region_w;
   if (B != 16 && B != 64 && B != 128) return DAP_E_UNSUPPORTED;
@@ -38,6 +40,22 @@ dap_status validate(const dap_config* c) {
   const long long bh = (long long)c->batch * c->heads;
   if (bh > 65535) return DAP_E_UNSUPPORTED;
   return DAP_OK;
+}
+
+// FNV-1a over every field of the configuration: the tag a workspace's stage word carries, so that
+// a stage left by a layer of another shape or quota is not taken for this one's.
+uint32_t config_tag(const dap_config* c) {
+  uint32_t h = 2166136261u;
+  auto mix = [&](const void* p, size_t n) {
+    const unsigned char* b = static_cast<const unsigned char*>(p);
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 16777619u;
+  };
+  const int32_t ints[] = {c->batch, c->heads, c->head_dim, c->T, c->H, c->W, c->region_h,
+                          c->region_w, c->quota_bp[0], c->quota_bp[1], c->quota_bp[2],
+                          c->quota_bp[3], c->fp4_format};
+  mix(ints, sizeof(ints));
+  mix(&c->lambda, sizeof(c->lambda));
+  return h;
 }
 
 void make_geo(const dap_config* c, Geo* g) {
@@ -69,6 +87,8 @@ void make_geo(const dap_config* c, Geo* g) {
   g->need16 = g->c16 > 0;
   g->need8 = g->c8 > g->c16;
   g->need4 = g->c4 > g->c8;
+  g->fp4_format = c->fp4_format;
+  g->tag = config_tag(c);
 }
 
 void make_layout(const Geo& g, dap_layout* L) {
@@ -122,6 +142,7 @@ void make_layout(const Geo& g, dap_layout* L) {
   L->off_out = take(bh * Np * D * 2);
   L->off_zeros = take(256);
   L->off_order = take((uint64_t)dap::kXcds * dap::xcd_stride(g.bh, g.Nb) * 4);
+  L->off_stage = take(8);
   L->total_bytes = o;
 }
 
@@ -156,6 +177,7 @@ Ws make_ws(void* base, const dap_layout& L) {
   w.out = reinterpret_cast<uint16_t*>(b + L.off_out);
   w.zeros = reinterpret_cast<uint8_t*>(b + L.off_zeros);
   w.order = reinterpret_cast<uint32_t*>(b + L.off_order);
+  w.stage = reinterpret_cast<uint32_t*>(b + L.off_stage);
   return w;
 }
 
@@ -210,9 +232,12 @@ dap_status dap_prepare(const dap_config* cfg, const void* q, const void* k, cons
   dap_status st = check_call(cfg, ws, ws_bytes, &g, &L);
   if (st != DAP_OK) return st;
   if (!q || !k || !v || !aligned(q) || !aligned(k) || !aligned(v)) return DAP_E_INVALID;
-  return hip_status(dap::launch_prepare(g, static_cast<const uint16_t*>(q),
-                                        static_cast<const uint16_t*>(k),
-                                        static_cast<const uint16_t*>(v), make_ws(ws, L), stream));
+  const Ws w = make_ws(ws, L);
+  hipError_t e = dap::launch_prepare(g, static_cast<const uint16_t*>(q),
+                                     static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), w, stream);
+  if (e == hipSuccess) e = dap::launch_stage(g, w, dap::kStageAny, DAP_STAGE_PREPARED, stream);
+  return hip_status(e);
 }
 
 dap_status dap_draft_rank(const dap_config* cfg, void* ws, size_t ws_bytes, uint8_t* map_out,
@@ -231,6 +256,11 @@ dap_status dap_draft_rank(const dap_config* cfg, void* ws, size_t ws_bytes, uint
   if (e == hipSuccess) e = dap::launch_rank(g, w, stream);
   if (e == hipSuccess && map_out)
     e = hipMemcpyAsync(map_out, w.map, (size_t)g.bh * g.pairs, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess)
+    e = dap::launch_stage(g, w,
+                          dap::stage_bit(DAP_STAGE_PREPARED) | dap::stage_bit(DAP_STAGE_RANKED) |
+                              dap::stage_bit(DAP_STAGE_ATTENDED),
+                          DAP_STAGE_RANKED, stream);
   return hip_status(e);
 }
 
@@ -239,7 +269,12 @@ dap_status dap_attention(const dap_config* cfg, void* ws, size_t ws_bytes, hipSt
   dap_layout L;
   dap_status st = check_call(cfg, ws, ws_bytes, &g, &L);
   if (st != DAP_OK) return st;
-  return hip_status(dap::launch_attention(g, make_ws(ws, L), stream));
+  const Ws w = make_ws(ws, L);
+  hipError_t e = dap::launch_attention(g, w, stream);
+  if (e == hipSuccess)
+    e = dap::launch_stage(g, w, dap::stage_bit(DAP_STAGE_RANKED) | dap::stage_bit(DAP_STAGE_ATTENDED),
+                          DAP_STAGE_ATTENDED, stream);
+  return hip_status(e);
 }
 
 dap_status dap_restore(const dap_config* cfg, const void* ws, size_t ws_bytes, void* out,

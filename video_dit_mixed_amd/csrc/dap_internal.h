@@ -17,6 +17,8 @@ struct Geo {
   long long pairs, c16, c8, c4;
   double lambda;
   int need16, need8, need4;  // does any pair use this precision
+  int fp4_format;            // DAP_FP4_*
+  uint32_t tag;              // configuration tag kept beside the stage word
 };
 
 // Device pointers to the workspace sections.
@@ -49,7 +51,23 @@ struct Ws {
   uint16_t* out;
   uint8_t* zeros;
   uint32_t* order;
+  uint32_t* stage;  // [0] stage word (DAP_STAGE_*), [1] configuration tag
 };
+
+// Stage words: DAP_STAGE_* = kStageMagic | stage number; `accept` masks of launch_stage are sets
+// of stage numbers (bit n = stage n accepted), kStageAny accepts anything (dap_prepare).
+constexpr uint32_t kStageMagic = 0xDA900000u;
+constexpr uint32_t kStageMagicMask = 0xFFFFFF00u;
+constexpr uint32_t kStageAny = 0xFFFFFFFFu;
+constexpr uint32_t stage_bit(uint32_t stage) { return 1u << (stage & 0xffu); }
+
+// True when the stage words (cur, t) show the result of the calls this one depends on: a stage in
+// `accept`, written under this configuration's tag.
+__host__ __device__ constexpr bool stage_ok(uint32_t cur, uint32_t t, uint32_t tag, uint32_t accept) {
+  return accept == kStageAny ||
+         (t == tag && (cur & kStageMagicMask) == kStageMagic && (cur & 0xffu) < 32u &&
+          ((accept >> (cur & 0xffu)) & 1u) != 0u);
+}
 
 // Ranking: an 87-bit key per pair, ascending key = (score descending, pair index ascending):
 //   key = ((~bits(score) & 0x7fff'ffff'ffff'ffff) << 24) | pair_index, pair_index < 2^24.
@@ -95,5 +113,6 @@ hipError_t launch_draft(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_rank(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_attention(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_restore(const Geo& g, const Ws& w, uint16_t* out, hipStream_t s);
+hipError_t launch_stage(const Geo& g, const Ws& w, uint32_t accept, uint32_t next, hipStream_t s);
 
 }  // namespace dap

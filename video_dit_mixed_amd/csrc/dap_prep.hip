@@ -2,21 +2,23 @@
 // quantisation of Q and K in one pass over each tensor; V absmax, then V reorder + transpose +
 // pack into the bf16 and FP8 matrix-core layouts.
 //
-// Method: "DraftAttention2" -- pchao.org blog, section 方法概览 bullet 4 (reorder, pooling and
-// quantisation of Q/K share one preparation kernel) and the Figure 3 caption (compact spatial
-// regions packed into contiguous blocks with gray padding; V reordering and transposition fused
-// with operand packing).  Pooling: section 方法概览 bullet 1 (average and channel-wise max
-// descriptor per region).
+// Method: "DraftAttention2" -- pchao.org blog, section 方法概览 bullet 4 (the reorder, the pooling
+// and the Q/K quantisation are done in the same preparation pass) and the Figure 3 caption (each
+// spatial region becomes one run of consecutive rows, padded where the frame ends; V is reordered
+// and transposed while its operands are packed).  Pooling: section 方法概览 bullet 1 (one mean and
+// one per-channel maximum per region).
 //
 // Number formats (exact, so codes match a reference bit for bit):
 //   INT8 per (head, block):   a = max|x| over the block, r = 127/a (fp32, correctly rounded),
-//                             code = clamp(rne(x*r), -127, 127), scale = a/127; a = 0 -> all 0.
+//                             code = clamp(rne(x*r), -127, 127), scale = a/127; a = 0, or r
+//                             overflowing to infinity (a below about 3.7e-37) -> all 0.
 //   MXFP4 per (row, 32 ch):   e = clamp(floor(log2 amax) - 2, -127, 127) (amax = 0 -> -127),
 //                             byte = e + 127, code = E2M1 rne saturating of x*2^-e, sign = sign
 //                             bit of x; two codes per byte, even channel in the low nibble.
 //   FP8 V per (head, ch):     a_d = max|V[:, d]| over real tokens, r = 448/a_d,
 //                             code = e4m3fn rne of x*r (|x*r| <= 448, so no saturation case;
-//                             the hardware converter v_cvt_pk_fp8_f32), scale = a_d/448.
+//                             the hardware converter v_cvt_pk_fp8_f32), scale = a_d/448; a_d = 0,
+//                             or r overflowing (a_d below about 1.3e-36) -> codes 0, scale 0.
 // Launch shapes: prep_qk one 256-thread workgroup per (block, head, tensor); v_amax a grid of
 // token slices per head; v_pack one workgroup per (block, head).  Reads are whole region rows
 // (region_w * D * 2 contiguous bytes) with 16-byte lanes.
@@ -188,7 +190,10 @@ __global__ __launch_bounds__(kThreads) void prep_qk_kernel(Geo g, const uint16_t
 
   // INT8 per block
   if (g.need8) {
-    const float r = amax > 0.0f ? 127.0f / amax : 0.0f;
+    // 127/0 is +inf as well: one test covers empty and vanishingly small blocks
+    const float r_raw = 127.0f / amax;
+    const bool zero_blk = !(r_raw <= 3.402823466e38f);
+    const float r = zero_blk ? 0.0f : r_raw;
     int8_t* dst = tensor == 0 ? w.q_i8 : w.k_i8;
 #pragma unroll
     for (int p = 0; p < MAXP; ++p) {
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void prep_qk_kernel(Geo g, const uint16_t
     }
     if (tid == 0) {
       float* sc = tensor == 0 ? w.q_i8_scale : w.k_i8_scale;
-      sc[(size_t)bh * g.Nb + b] = amax > 0.0f ? amax / 127.0f : 0.0f;
+      sc[(size_t)bh * g.Nb + b] = zero_blk ? 0.0f : amax / 127.0f;
     }
   }
 
@@ -327,8 +332,10 @@ __global__ __launch_bounds__(kThreads) void v_pack_kernel(Geo g, const uint16_t*
 
   if (tid < D) {
     const float a = __uint_as_float(w.v_amax[(size_t)bh * D + tid]);
-    s_r[tid] = a > 0.0f ? 448.0f / a : 0.0f;
-    if (b == 0) w.v_scale[(size_t)bh * D + tid] = a > 0.0f ? a / 448.0f : 0.0f;
+    const float r = 448.0f / a;  // +inf for a = 0 and for vanishingly small channels
+    const bool zero_ch = !(r <= 3.402823466e38f);
+    s_r[tid] = zero_ch ? 0.0f : r;
+    if (b == 0) w.v_scale[(size_t)bh * D + tid] = zero_ch ? 0.0f : a / 448.0f;
   }
   // gather: key r of the block is region pixel (iy, ix) = (r / rw, r % rw); pad keys are 0.
   // Every load of the thread is issued before the first LDS store.
@@ -388,7 +395,8 @@ __global__ __launch_bounds__(kThreads) void v_pack_kernel(Geo g, const uint16_t*
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = vt8_key(16 * cc + 4 * j + e);
-          x[e] = key < B ? bf16_to_f32(val(key, d)) * r : 0.0f;
+          // a zero channel (r = 0) gets code +0 everywhere, not the sign of x * 0
+          x[e] = key < B && r != 0.0f ? bf16_to_f32(val(key, d)) * r : 0.0f;
         }
         int word = (int)__float_as_uint(x[0]);  // any value: both halves are written below
         word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], word, false);

@@ -11,7 +11,11 @@ namespace dap {
 namespace {
 
 __global__ __launch_bounds__(256) void restore_kernel(Geo g, const uint16_t* __restrict__ packed,
+                                                      const uint32_t* __restrict__ stage,
                                                       uint16_t* __restrict__ out) {
+  // the packed output is only copied once attention has run on this workspace for this
+  // configuration; otherwise the output is zeros
+  const bool ok = stage_ok(stage[0], stage[1], g.tag, stage_bit(DAP_STAGE_ATTENDED));
   const int CH = g.D / 8;
   const size_t total = (size_t)g.bh * g.N * CH;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -28,7 +32,8 @@ __global__ __launch_bounds__(256) void restore_kernel(Geo g, const uint16_t* __r
     const int rx = x / g.rw, ix = x - rx * g.rw;
     const size_t b = ((size_t)t * g.nby + ry) * g.nbx + rx;
     const size_t p = b * g.B + (size_t)iy * g.rw + ix;
-    const uint4 v = *reinterpret_cast<const uint4*>(packed + ((size_t)bh * g.Np + p) * g.D + c * 8);
+    const uint4 v = ok ? *reinterpret_cast<const uint4*>(packed + ((size_t)bh * g.Np + p) * g.D + c * 8)
+                       : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(out + tok * g.D + c * 8) = v;
   }
 }
@@ -38,7 +43,7 @@ __global__ __launch_bounds__(256) void restore_kernel(Geo g, const uint16_t* __r
 hipError_t launch_restore(const Geo& g, const Ws& w, uint16_t* out, hipStream_t s) {
   const size_t total = (size_t)g.bh * g.N * (g.D / 8);
   const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 * 4 ? (total + 255) / 256 : 65536 * 4);
-  restore_kernel<<<blocks, 256, 0, s>>>(g, w.out, out);
+  restore_kernel<<<blocks, 256, 0, s>>>(g, w.out, w.stage, out);
   return hipGetLastError();
 }
 
