@@ -89,7 +89,8 @@ typedef enum {
   DAP_E_INVALID = 1,
   DAP_E_UNSUPPORTED = 2,
   DAP_E_WORKSPACE = 3,
-  DAP_E_HIP = 4
+  DAP_E_HIP = 4,
+  DAP_E_SCRATCH_LIMIT = 5 /* dap_prepare_static_scratch: batch*heads*head_dim above 65536 */
 } dap_status;
 
 typedef struct {
@@ -157,6 +158,20 @@ dap_status dap_workspace_layout(const dap_config* cfg, dap_layout* out);
  * Formats of a precision whose quota is 0 are not written. */
 dap_status dap_prepare(const dap_config* cfg, const void* q, const void* k, const void* v,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): dap_prepare with its scratch -- the per-channel V
+ * maxima, batch*heads*head_dim 32-bit words -- held in a static device array of the library
+ * (65536 words, 256 KiB, one copy per device, kept until the process ends) instead of the
+ * workspace's v_amax section, which it leaves untouched.  Same arguments, results and errors as
+ * dap_prepare, plus DAP_E_SCRATCH_LIMIT when batch*heads*head_dim exceeds 65536.  It allocates
+ * nothing: the array's device address is looked up once per device (hipGetSymbolAddress) on the
+ * first call made with that device current; `stream` must belong to the current device.  All
+ * calls on one device share the array and each clears it before use, so calls that can overlap
+ * on one device (other streams, other host threads) race and must be serialised by the caller. */
+dap_status dap_prepare_static_scratch(const dap_config* cfg, const void* q, const void* k,
+                                      const void* v, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
 
 /* Draft map (pooled Q K^T / sqrt(D), row softmax over key regions, (1-lambda)*avg + lambda*max),
  * per-head ranking and 4-level block map with per-row key-block lists.  map_out (uint8

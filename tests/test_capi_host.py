@@ -83,6 +83,20 @@ def test_calls_validate_before_touching_the_device():
     assert lib.dap_restore(P(c), 256, need, None, None) == b.DAP_E_INVALID
     bad = _cfg(head_dim=32).c_struct()
     assert lib.dap_attention(P(bad), 256, need, None) == b.DAP_E_UNSUPPORTED
+    assert lib.dap_prepare_static_scratch(P(c), None, 256, 256, 256, need, None) == b.DAP_E_INVALID
+    assert lib.dap_prepare_static_scratch(P(c), 256, 256, 256, 256, need - 1, None) == b.DAP_E_WORKSPACE
+
+
+def test_static_scratch_limit_is_checked_on_the_host():
+    """batch * heads * head_dim above the static array (65536 words) is refused before any HIP call."""
+    lib = b.load()
+    cfg = b.Config(batch=1, heads=513, head_dim=128, T=1, H=8, W=16, region_h=8, region_w=16,
+                   lam=0.5, quota_bp=(0, 0, 0, 10000))
+    c = cfg.c_struct()
+    need = b.workspace_bytes(cfg)
+    assert lib.dap_prepare_static_scratch(ctypes.byref(c), 256, 256, 256, 256, need, None) == \
+        b.DAP_E_SCRATCH_LIMIT
+    assert "static scratch" in b.status_string(b.DAP_E_SCRATCH_LIMIT)
 
 
 def _layout_py(w):

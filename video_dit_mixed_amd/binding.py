@@ -17,14 +17,15 @@ from typing import Optional, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdap.so")
 
-DAP_OK, DAP_E_INVALID, DAP_E_UNSUPPORTED, DAP_E_WORKSPACE, DAP_E_HIP = range(5)
+DAP_OK, DAP_E_INVALID, DAP_E_UNSUPPORTED, DAP_E_WORKSPACE, DAP_E_HIP, DAP_E_SCRATCH_LIMIT = range(6)
 ABI_VERSION = 2
 STAGE_PREPARED, STAGE_RANKED, STAGE_ATTENDED, STAGE_BROKEN = (0xDA900001, 0xDA900002, 0xDA900003,
                                                               0xDA9000FF)
 FP4_MXFP4, FP4_NVFP4 = 0, 1
 LEVEL_SKIP, LEVEL_4, LEVEL_8, LEVEL_16 = 0, 1, 2, 3
 EXPORTED = ("dap_abi_version", "dap_workspace_bytes", "dap_workspace_layout", "dap_prepare",
-            "dap_draft_rank", "dap_attention", "dap_restore", "dap_status_string")
+            "dap_prepare_static_scratch", "dap_draft_rank", "dap_attention", "dap_restore",
+            "dap_status_string")
 
 
 class DapError(RuntimeError):
@@ -114,6 +115,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.dap_prepare.restype = ctypes.c_int
     lib.dap_prepare.argtypes = [P(_Config), vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.dap_prepare_static_scratch.restype = ctypes.c_int
+    lib.dap_prepare_static_scratch.argtypes = [P(_Config), vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.dap_draft_rank.restype = ctypes.c_int
     lib.dap_draft_rank.argtypes = [P(_Config), vp, ctypes.c_size_t, vp, vp, vp]
     lib.dap_attention.restype = ctypes.c_int
@@ -216,6 +219,17 @@ def prepare(cfg: Config, q, k, v, ws, stream=None):
     c = cfg.c_struct()
     _check(load().dap_prepare(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(ws), _nbytes(ws),
                               _stream(stream)), "dap_prepare")
+
+
+def prepare_static_scratch(cfg: Config, q, k, v, ws, stream=None):
+    """dap_prepare with its scratch in the library's static device array (no allocation)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, name, "bfloat16", _io_shape(cfg))
+    _expect(ws, "ws", "uint8")
+    c = cfg.c_struct()
+    _check(load().dap_prepare_static_scratch(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(ws),
+                                             _nbytes(ws), _stream(stream)),
+           "dap_prepare_static_scratch")
 
 
 def draft_rank(cfg: Config, ws, map_out=None, scores_out=None, stream=None):

@@ -240,6 +240,23 @@ dap_status dap_prepare(const dap_config* cfg, const void* q, const void* k, cons
   return hip_status(e);
 }
 
+dap_status dap_prepare_static_scratch(const dap_config* cfg, const void* q, const void* k,
+                                      const void* v, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  Geo g;
+  dap_layout L;
+  dap_status st = check_call(cfg, ws, ws_bytes, &g, &L);
+  if (st != DAP_OK) return st;
+  if (!q || !k || !v || !aligned(q) || !aligned(k) || !aligned(v)) return DAP_E_INVALID;
+  if ((size_t)g.bh * g.D > dap::kStaticScratchWords) return DAP_E_SCRATCH_LIMIT;
+  const Ws w = make_ws(ws, L);
+  hipError_t e = dap::launch_prepare_static_scratch(g, static_cast<const uint16_t*>(q),
+                                                    static_cast<const uint16_t*>(k),
+                                                    static_cast<const uint16_t*>(v), w, stream);
+  if (e == hipSuccess) e = dap::launch_stage(g, w, dap::kStageAny, DAP_STAGE_PREPARED, stream);
+  return hip_status(e);
+}
+
 dap_status dap_draft_rank(const dap_config* cfg, void* ws, size_t ws_bytes, uint8_t* map_out,
                           double* scores_out, hipStream_t stream) {
   Geo g;
@@ -295,6 +312,7 @@ const char* dap_status_string(dap_status s) {
     case DAP_E_UNSUPPORTED: return "unsupported configuration";
     case DAP_E_WORKSPACE: return "workspace too small";
     case DAP_E_HIP: return "HIP launch failure";
+    case DAP_E_SCRATCH_LIMIT: return "batch * heads * head_dim exceeds the static scratch (65536)";
   }
   return "unknown status";
 }

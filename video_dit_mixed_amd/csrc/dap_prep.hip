@@ -24,6 +24,8 @@
 // (region_w * D * 2 contiguous bytes) with 16-byte lanes.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "dap_internal.h"
 
 namespace dap {
@@ -433,6 +435,47 @@ hipError_t prepare_d(const Geo& g, const uint16_t* q, const uint16_t* k, const u
 hipError_t launch_prepare(const Geo& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           const Ws& w, hipStream_t s) {
   return g.D == 64 ? prepare_d<64>(g, q, k, v, w, s) : prepare_d<128>(g, q, k, v, w, s);
+}
+
+// ------------------------------------------------------------------------------------ static scratch
+// The per-channel V maxima are the preparation's only scratch (written by v_amax_kernel, read by
+// v_pack_kernel in the same call).  dap_prepare_static_scratch keeps them in this array instead
+// of the caller's workspace.  Each device that loads the library holds its own copy until the
+// process ends; its address on the current device comes from hipGetSymbolAddress, taken once per
+// device.  In host code `scratch` names a host-side stand-in, never a device address.
+static __device__ __align__(256) uint32_t scratch[kStaticScratchWords];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(uint32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_prepare_static_scratch(const Geo& g, const uint16_t* q, const uint16_t* k,
+                                         const uint16_t* v, const Ws& w, hipStream_t s) {
+  if ((size_t)g.bh * g.D > kStaticScratchWords) return hipErrorInvalidValue;  // checked by the caller
+  uint32_t* p = nullptr;
+  const hipError_t e = static_scratch(&p);
+  if (e != hipSuccess) return e;
+  Ws ws = w;
+  ws.v_amax = p;  // cleared by prepare's own fill kernel before the maxima are taken
+  return launch_prepare(g, q, k, v, ws, s);
 }
 
 }  // namespace dap
