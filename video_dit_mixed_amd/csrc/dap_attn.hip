@@ -454,7 +454,8 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
                 p[e] = __builtin_amdgcn_exp2f(fmaf(S[mt < C::MT ? mt : 0][4 * q4 + e], cs, nbias));
                 psum += p[e];
               }
-              word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+              // the old-value operand is any register: both halves are written
+              word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
               word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
             }
             bop[4 * hsel + q4] = word;
