@@ -10,7 +10,7 @@ Per query block qb, over its real query rows, with running max m = -inf, sum l =
   for phase in (16-bit, 8-bit, 4-bit), for each key block kb of that level in ascending order:
     S  = 16-bit: Q_bf16 K_bf16^T / sqrt(D)
           8-bit: (q_codes . k_codes) * s_q * s_k / sqrt(D)
-          4-bit: (MXFP4-dequantised Q . MXFP4-dequantised K) / sqrt(D)
+          4-bit: (dequantised 4-bit Q . dequantised 4-bit K) / sqrt(D), MXFP4 or NVFP4
     pad keys of kb get -inf
     m' = max(m, rowmax S); alpha = exp(m - m'); P = exp(S - m'); l = alpha*l + rowsum P
     16-bit: O = alpha*O + bf16(P) V_bf16

@@ -50,7 +50,14 @@ class HeadResult:
     k_e8: np.ndarray
     v_fp8: np.ndarray                 # [Np, D] uint8 e4m3fn codes
     v_s: np.ndarray                   # [D] f32
-    q_fp4_val: np.ndarray = None      # dequantised MXFP4 (exact fp64)
+    fp4_format: str = "mxfp4"         # 4-bit operands: "mxfp4" or "nvfp4" (R17 / R30)
+    q_nv: np.ndarray = None           # NVFP4 codes [Np, D] 0..15, E4M3 scale bytes [Np, D/16], tensor scale
+    q_nv_s: np.ndarray = None
+    q_nv_t: np.float32 = None
+    k_nv: np.ndarray = None
+    k_nv_s: np.ndarray = None
+    k_nv_t: np.float32 = None
+    q_fp4_val: np.ndarray = None      # dequantised 4-bit operands (exact fp64)
     k_fp4_val: np.ndarray = None
     v_fp8_val: np.ndarray = None      # V_fp8 * s_V (exact fp64)
     levels_override: Optional[np.ndarray] = None
@@ -81,8 +88,9 @@ class _Ops:
 
 
 def prepare_head(q_bits, k_bits, v_bits, *, T, H, W, rh, rw, lam, quota_bp,
-                 levels_override=None) -> HeadResult:
-    """Every step up to (not including) attention for one head.  q/k/v_bits: [N, D] bf16 bits."""
+                 levels_override=None, fp4_format: str = "mxfp4") -> HeadResult:
+    """Every step up to (not including) attention for one head.  q/k/v_bits: [N, D] bf16 bits.
+    fp4_format: the 4-bit level's operands, OCP MXFP4 (R17) or NVFP4 (R30)."""
     g = layout.geometry(T, H, W, rh, rw)
     q = bf16_bits_to_f64(q_bits)
     k = bf16_bits_to_f64(k_bits)
@@ -114,8 +122,18 @@ def prepare_head(q_bits, k_bits, v_bits, *, T, H, W, rh, rw, lam, quota_bp,
     r = HeadResult(g, D, B, valid, qp, kp, vp, q_avg, q_max, k_avg, k_max, A, A_avg, A_max,
                    rank, cuts, levels, q_i8, q_i8_s, k_i8, k_i8_s, q_fp4, q_e8, k_fp4, k_e8,
                    v_fp8, v_s)
-    r.q_fp4_val = quant.mxfp4_decode(q_fp4, q_e8)
-    r.k_fp4_val = quant.mxfp4_decode(k_fp4, k_e8)
+    r.fp4_format = fp4_format
+    if fp4_format == "nvfp4":
+        # one tensor scale per (head, tensor): amax over the packed rows = over the real tokens
+        r.q_nv, r.q_nv_s, r.q_nv_t = quant.nvfp4(qp)
+        r.k_nv, r.k_nv_s, r.k_nv_t = quant.nvfp4(kp)
+        r.q_fp4_val = quant.nvfp4_decode(r.q_nv, r.q_nv_s, r.q_nv_t)
+        r.k_fp4_val = quant.nvfp4_decode(r.k_nv, r.k_nv_s, r.k_nv_t)
+    elif fp4_format == "mxfp4":
+        r.q_fp4_val = quant.mxfp4_decode(q_fp4, q_e8)
+        r.k_fp4_val = quant.mxfp4_decode(k_fp4, k_e8)
+    else:
+        raise ValueError(fp4_format)
     r.v_fp8_val = quant.e4m3fn_decode(v_fp8) * v_s.astype(np.float64)[None, :]
     r.levels_override = levels_override
     r.out_packed = np.full((g.Np, D), np.nan)
@@ -135,14 +153,15 @@ def attend(r: HeadResult, q_blocks=None, emulate_p_rounding: bool = True) -> Hea
 
 
 def run_head(q_bits, k_bits, v_bits, *, T, H, W, rh, rw, lam, quota_bp, q_blocks=None,
-             emulate_p_rounding: bool = True, levels_override=None) -> HeadResult:
+             emulate_p_rounding: bool = True, levels_override=None,
+             fp4_format: str = "mxfp4") -> HeadResult:
     r = prepare_head(q_bits, k_bits, v_bits, T=T, H=H, W=W, rh=rh, rw=rw, lam=lam,
-                     quota_bp=quota_bp, levels_override=levels_override)
+                     quota_bp=quota_bp, levels_override=levels_override, fp4_format=fp4_format)
     return attend(r, q_blocks, emulate_p_rounding)
 
 
 def run(Q, K, V, *, T, H, W, rh, rw, lam, quota_bp, heads=None, q_blocks=None,
-        emulate_p_rounding: bool = True):
+        emulate_p_rounding: bool = True, fp4_format: str = "mxfp4"):
     """Q/K/V: [batch, heads, N, D] bf16 bits.  Returns {(b, h): HeadResult}."""
     out = {}
     Bt, Hh = Q.shape[:2]
@@ -150,5 +169,5 @@ def run(Q, K, V, *, T, H, W, rh, rw, lam, quota_bp, heads=None, q_blocks=None,
     for b, h in idx:
         out[(b, h)] = run_head(Q[b, h], K[b, h], V[b, h], T=T, H=H, W=W, rh=rh, rw=rw, lam=lam,
                                quota_bp=quota_bp, q_blocks=q_blocks,
-                               emulate_p_rounding=emulate_p_rounding)
+                               emulate_p_rounding=emulate_p_rounding, fp4_format=fp4_format)
     return out

@@ -15,6 +15,8 @@ Readings:
       E2M1 codes, RNE, saturating at 6.  (The pages name NVFP4 as an example; MXFP4 is the 4-bit
       format the gfx950 scaled matrix cores consume.)
   R20 FP8 V: one fp32 scale per (head, channel) over real tokens; e4m3fn codes, RNE, saturating.
+  R30 NVFP4 (selectable instead of MXFP4): groups of 16 channels, E4M3 group scales, one fp32
+      scale per (head, tensor) over real tokens; the fp32 steps are listed at nvfp4().
   R26 all-zero blocks / groups / channels: INT8 codes 0 with scale 0; MX exponent -127;
       FP8 codes 0 with scale 0.  A block or channel whose maximum is so small that the fp32
       reciprocal of the quantiser (127/a, 448/a) overflows is treated the same way (below about
@@ -167,33 +169,64 @@ def mxfp4_decode(codes: np.ndarray, e8m0: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
-# NVFP4 (the pages' 4-bit example format; a comparison format, not on the GPU path)
+# NVFP4: the pages' example 4-bit format (pchao.org blog, section 方法概览 bullet 2: the low-bit
+# level is, for example, NVFP4) -- E2M1 elements in groups of 16 consecutive channels, each group
+# scaled by an E4M3 factor, on top of one fp32 factor for the whole tensor.  The two-level scaling
+# is the format's definition; the fp32 order of the steps is reading R30.
+
+NV_GROUP = 16
+NV_TOP = F32(6.0 * 448.0)   # largest E2M1 value times largest E4M3 value
+
+
+def nvfp4(x: np.ndarray, amax=None):
+    """NVFP4 of rows x [..., D] (fp64 values of bf16 inputs), one tensor scale for all of x.
+
+    amax = max|x| over the tensor (default: over x itself; pad rows are 0 and do not change it).
+    R30, every step in fp32 (numpy float32 is correctly rounded):
+      t    = f32(amax / 2688)                   tensor scale; 0 -> every code and scale is 0
+      d    = f32(6 * t)
+      s_g  = e4m3fn_rne_sat(f32(a_g / d))       group scale, a_g = max|x| over the group's 16
+      step = f32(s_g * t);  inv = f32(1 / step) (0 when step is 0 or inv is not finite: the
+                                                 group's codes are then 0)
+      code = E2M1_rne_sat(f32(|x| * inv)), bit 3 = the IEEE sign bit of x
+    Returns (codes uint8 [..., D] 0..15, scale bytes uint8 [..., D/16] (e4m3fn), t float32)."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    if amax is None:
+        amax = float(np.max(np.abs(x))) if x.size else 0.0
+    t = F32(F32(amax) / NV_TOP)
+    shape_g = x.shape[:-1] + (D // NV_GROUP,)
+    if t == 0:
+        return np.zeros(x.shape, np.uint8), np.zeros(shape_g, np.uint8), F32(0.0)
+    d = F32(F32(6.0) * t)
+    xg = x.reshape(x.shape[:-1] + (D // NV_GROUP, NV_GROUP))
+    a_g = np.max(np.abs(xg), axis=-1).astype(F32)
+    sg_val = e4m3fn_rne_sat((a_g / d).astype(F32).astype(np.float64))
+    sg_code = e4m3fn_encode(sg_val, np.zeros(sg_val.shape, bool))
+    step = (sg_val.astype(F32) * t).astype(F32)
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = np.where(step > 0, F32(1.0) / np.where(step > 0, step, F32(1.0)), F32(0.0)).astype(F32)
+    inv = np.where(np.isfinite(inv), inv, F32(0.0)).astype(F32)
+    scaled = (np.abs(xg).astype(F32) * inv[..., None]).astype(F32)
+    mag = e2m1_rne_sat(scaled.astype(np.float64))
+    sign = np.signbit(xg).astype(np.uint8) << 3
+    codes = (mag | sign).reshape(x.shape)
+    return codes, sg_code, t
+
+
+def nvfp4_decode(codes: np.ndarray, sg_code: np.ndarray, t) -> np.ndarray:
+    """Values of NVFP4 codes (exact fp64): E2M1 value x E4M3 group scale x tensor scale."""
+    c = np.asarray(codes, dtype=np.int64)
+    v = E2M1_GRID[c & 7] * np.where(c & 8, -1.0, 1.0)
+    D = c.shape[-1]
+    vg = v.reshape(c.shape[:-1] + (D // NV_GROUP, NV_GROUP))
+    sg = e4m3fn_decode(sg_code)
+    return (vg * sg[..., None] * float(t)).reshape(c.shape)
 
 
 def nvfp4_dequant(x: np.ndarray) -> np.ndarray:
-    """NVFP4 round trip of rows x [..., D] (fp64 values of bf16): E2M1 elements in groups of 16
-    consecutive channels, each group scaled by an E4M3 factor, on top of one fp32 factor for the
-    whole tensor (pchao.org blog, section 方法概览 bullet 2: the low-bit level is, for example,
-    NVFP4).  Written from the two-level scaling the format defines:
-      s_t = amax(x) / (6 * 448)                        (fp64; the tensor's largest value maps to
-                                                        the largest element times the largest scale)
-      s_g = e4m3fn_rne_sat(amax(group) / (6 * s_t))    (group scale on the E4M3 grid)
-      v   = sign(x) * E2M1_rne_sat(|x| / step) * step,  step = s_g * s_t   (0 for a zero scale)
-    Returns the dequantised fp64 values (same shape)."""
-    x = np.asarray(x, dtype=np.float64)
-    D = x.shape[-1]
-    amax_t = float(np.max(np.abs(x))) if x.size else 0.0
-    if amax_t == 0.0:
-        return np.zeros_like(x)
-    s_t = amax_t / (6.0 * 448.0)
-    xg = x.reshape(x.shape[:-1] + (D // 16, 16))
-    s_g = e4m3fn_rne_sat(np.max(np.abs(xg), axis=-1) / (6.0 * s_t))
-    step = s_g * s_t
-    with np.errstate(divide="ignore", invalid="ignore"):
-        scaled = np.where(step[..., None] > 0, np.abs(xg) / step[..., None], 0.0)
-    mag = E2M1_GRID[e2m1_rne_sat(scaled)]
-    v = np.where(np.signbit(xg), -mag, mag) * step[..., None]
-    return v.reshape(x.shape)
+    """NVFP4 round trip of rows x [..., D] with the tensor scale taken over x (quality sweep)."""
+    return nvfp4_decode(*nvfp4(x))
 
 
 # ----------------------------------------------------------------------------------------------

@@ -234,43 +234,126 @@ def test_fp8_v_reciprocal_overflow_is_a_zero_channel():
     assert np.all(np.isfinite(quant.e4m3fn_decode(codes[:, ok])))
 
 
-def test_nvfp4_matches_brute_force_nearest_grid_point():
-    """Each NVFP4 value is the nearest point of its group's grid {+-E2M1 * step}, step = s_g s_t
-    (ties to the even code), with s_g the E4M3 rounding of amax/(6 s_t); found here by exhaustive
-    search."""
+def _f32_rne(x: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a non-negative rational to fp32, zero and subnormals
+    included (quantum 2^-149 below 2^-126)."""
+    if x == 0:
+        return Fraction(0)
+    e = math.floor(math.log2(x))
+    while Fraction(2) ** e > x:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= x:
+        e += 1
+    q = Fraction(2) ** (max(e, -126) - 23)
+    n = x / q
+    fl = math.floor(n)
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl * q
+
+
+def _e4m3_torch(v: float) -> float:
+    """torch's own e4m3fn cast (round to nearest even, saturating the finite range here)."""
+    return float(torch.tensor([min(v, 448.0)], dtype=torch.float32).to(torch.float8_e4m3fn).float())
+
+
+def _nvfp4_reference(x):
+    """NVFP4 of x by exact rational arithmetic, each fp32 step rounded to nearest even by hand, the
+    E4M3 step by torch's float8 cast, and every code by searching the E2M1 grid for the nearest
+    value (ties to the even code).  Returns (codes, group scale values, t)."""
+    grid = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+            Fraction(4), Fraction(6)]
+    amax = max(abs(Fraction(float(v))) for v in x.ravel())
+    t = _f32_rne(amax / 2688)
+    codes = np.zeros(x.shape, np.uint8)
+    sgs = np.zeros(x.shape[:-1] + (x.shape[-1] // 16,))
+    if t == 0:
+        return codes, sgs, t
+    d = _f32_rne(6 * t)
+    for idx in np.ndindex(x.shape[:-1]):
+        for g in range(x.shape[-1] // 16):
+            blk = [Fraction(float(v)) for v in x[idx + (slice(16 * g, 16 * g + 16),)]]
+            a_g = max(abs(v) for v in blk)
+            sg = Fraction(_e4m3_torch(float(_f32_rne(a_g / d))))
+            sgs[idx + (g,)] = float(sg)
+            step = _f32_rne(sg * t)
+            if step == 0:
+                continue
+            inv = _f32_rne(1 / step)
+            for i, v in enumerate(blk):
+                y = _f32_rne(abs(v) * inv)
+                dist = [abs(y - gv) for gv in grid]
+                best = [k for k, dd in enumerate(dist) if dd == min(dist)]
+                k = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+                neg = np.signbit(x[idx + (16 * g + i,)])
+                codes[idx + (16 * g + i,)] = k | (8 if neg else 0)
+    return codes, sgs, t
+
+
+def test_nvfp4_matches_exact_step_by_step_reference():
+    """Tensor scale, group scales and codes equal an exact rational evaluation of the same fp32
+    steps (R30), with the E4M3 rounding taken from torch and the E2M1 rounding from a nearest-grid
+    search; inputs span several binades, a zero group, an outlier and negative zeros."""
     rng = np.random.default_rng(11)
-    x = (rng.standard_normal((6, 64)) * np.exp(rng.uniform(-4, 4, (6, 1)))).astype(np.float64)
+    x = quant.bf16_rne(rng.standard_normal((5, 64)) * np.exp(rng.uniform(-4, 4, (5, 1))))
     x[2, 16:32] = 0.0                       # an all-zero group
     x[3, 5] = 40.0                          # an outlier sets the tensor scale
-    got = quant.nvfp4_dequant(x)
-    s_t = np.abs(x).max() / (6 * 448)
-    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
-    for r in range(x.shape[0]):
-        for g in range(4):
-            blk = x[r, 16 * g:16 * g + 16]
-            s_g = quant.e4m3fn_rne_sat(np.array([np.abs(blk).max() / (6 * s_t)]))[0]
-            for i, v in enumerate(blk):
-                if s_g == 0:
-                    assert got[r, 16 * g + i] == 0.0
-                    continue
-                cand = grid * (s_g * s_t)      # the group's grid: E2M1 values times its step
-                d = np.abs(np.abs(v) - cand)
-                best = np.flatnonzero(d == d.min())
-                k = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
-                exp = np.copysign(cand[k], v) if cand[k] != 0 else (np.copysign(0.0, v))
-                assert got[r, 16 * g + i] == exp, (r, g, i, v, got[r, 16 * g + i], exp)
+    x[4, 7] = -0.0
+    codes, sg_code, t = quant.nvfp4(x)
+    rc, rsg, rt = _nvfp4_reference(x)
+    assert Fraction(float(t)) == rt
+    np.testing.assert_array_equal(quant.e4m3fn_decode(sg_code), rsg)
+    np.testing.assert_array_equal(codes, rc)
+    # decoding: E2M1 value x group scale x tensor scale
+    v = quant.nvfp4_decode(codes, sg_code, t)
+    grid = quant.E2M1_GRID
+    exp = np.where(rc & 8, -1.0, 1.0) * grid[rc & 7] * np.repeat(rsg, 16, axis=-1) * float(rt)
+    np.testing.assert_array_equal(v, exp)
 
 
-def test_nvfp4_exact_on_representable_values_and_saturates():
-    # values already on a group's grid come back unchanged: pick s_t from the tensor max, a group
-    # scale on the e4m3 grid, elements on the E2M1 grid
-    s_t = 6.0 / (6 * 448)                     # tensor max 6 -> s_t = 1/448
+def test_nvfp4_codes_exhaustive_over_bf16():
+    """Every finite bf16 value inside a tensor whose scales are fixed by two anchor elements gets the
+    code of the exact step-by-step reference."""
+    vals = _all_finite_bf16()
+    vals = vals[np.abs(vals) <= 2.0 ** 6]
+    n = (vals.size + 13) // 14 * 14
+    body = np.zeros(n)
+    body[:vals.size] = vals
+    rows = body.reshape(-1, 14)
+    anchors = np.tile([2.0 ** 6, -1.5], (rows.shape[0], 1))  # tensor amax 64; every group has 1.5
+    x = np.concatenate([rows, anchors], axis=1)               # groups of 16 = one row each
+    codes, sg_code, t = quant.nvfp4(x)
+    d = Fraction(float(quant.F32(6) * t))
+    assert Fraction(float(t)) == _f32_rne(Fraction(64) / 2688)
+    grid = [Fraction(v) for v in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    sgv = quant.e4m3fn_decode(sg_code)[:, 0]
+    for r in range(rows.shape[0]):           # every row: every value, and a spread of group maxima
+        a_g = max(abs(Fraction(float(v))) for v in x[r])
+        assert sgv[r] == _e4m3_torch(float(_f32_rne(a_g / d)))
+        step = _f32_rne(Fraction(float(sgv[r])) * Fraction(float(t)))
+        inv = _f32_rne(1 / step)
+        for i in range(16):
+            y = _f32_rne(abs(Fraction(float(x[r, i]))) * inv)
+            dist = [abs(y - gv) for gv in grid]
+            best = [k for k, dd in enumerate(dist) if dd == min(dist)]
+            k = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            assert codes[r, i] & 7 == k and (codes[r, i] >> 3) == int(np.signbit(x[r, i])), (r, i)
+
+
+def test_nvfp4_exact_on_representable_values_and_zero_tensor():
+    # values already on a group's grid come back unchanged: amax = 2688 * 2^-9 makes t = 2^-9 and
+    # the group scales 448 and 224 exact; elements on the E2M1 grid times the step
     grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
-    row = np.concatenate([grid, -grid[::-1]]) * 448 * s_t   # group scale 448 (largest) -> max 6
-    x = np.stack([row, row * 0.5])            # second group: scale 224 (on the e4m3 grid)
+    t = 2.0 ** -9
+    row = np.concatenate([grid, -grid[::-1]]) * 448 * t
+    x = np.stack([row, row * 0.5])
     np.testing.assert_array_equal(quant.nvfp4_dequant(x), x)
-    # the largest element of every group maps to at most 6 * s_g * s_t
+    c, s, t0 = quant.nvfp4(np.zeros((2, 32)))
+    assert t0 == 0 and not c.any() and not s.any()
+    # the element that sets the tensor scale maps to +-6 x 448 x t, the top of the format
     rng = np.random.default_rng(3)
-    y = rng.standard_normal((4, 32))
-    v = quant.nvfp4_dequant(y)
-    assert np.all(np.abs(v) <= np.abs(y).max() * (1 + 2 ** -3) + 1e-12)
+    y = quant.bf16_rne(rng.standard_normal((4, 32)))
+    codes, sg_code, tt = quant.nvfp4(y)
+    i = np.unravel_index(np.argmax(np.abs(y)), y.shape)
+    assert codes[i] & 7 == 7 and quant.e4m3fn_decode(sg_code[i[0], i[1] // 16]) == 448.0
