@@ -53,8 +53,7 @@
  *   Host-side validation runs before any HIP call and returns DAP_E_INVALID (null pointer, bad
  *   size, lambda outside [0, 1], negative quota or quota sum above 10000, misaligned pointer),
  *   DAP_E_UNSUPPORTED (head_dim not 64/128, region size not 16/64/128 tokens, more than 4096
- *   regions per head, an fp4_format this build does not provide) or DAP_E_WORKSPACE (ws_bytes
- *   too small).  A failed kernel launch returns
+ *   regions per head) or DAP_E_WORKSPACE (ws_bytes too small).  A failed kernel launch returns
  *   DAP_E_HIP.  Device faults surface at the caller's next synchronisation.  Non-finite inputs
  *   are outside the contract.
  */
@@ -113,6 +112,13 @@ typedef struct {
  *   q_i8, k_i8      [bh][Np][D] int8 codes;  q_i8_scale, k_i8_scale [bh][Nb] fp32
  *   q_fp4, k_fp4    [bh][Np][D/2] E2M1 codes, two per byte, even channel in the low nibble
  *   q_e8m0, k_e8m0  [bh][Np][D/32] E8M0 exponents (value 2^(byte-127)) per 32-channel group
+ *                   (fp4_format MXFP4; with NVFP4, q_fp4 / k_fp4 hold the NVFP4 E2M1 codes)
+ *   q_nv_scale, k_nv_scale  [bh][Np][D/16] e4m3fn group scales of NVFP4 (empty for MXFP4)
+ *   q_nv_bf16, k_nv_bf16    [bh][Np][D] bf16: NVFP4 values without the tensor scale (E2M1 value x
+ *                   group scale, exact in bf16), the operands of the 4-bit Q K^T (empty for MXFP4)
+ *   nv_tscale       [bh][2] fp32 NVFP4 tensor scales of Q and K (empty for MXFP4)
+ *   qk_amax         [2][bh][D] uint32 (fp32 bits): per-channel maxima of |Q| and |K|, scratch of
+ *                   the NVFP4 tensor scale (empty for MXFP4)
  *   vt_fp8          [bh][Nb][D][kp8] e4m3fn codes of V transposed per block, kp8 = B rounded up to
  *                   64; inside each 64-key chunk position 32*g + j holds key
  *                   32*(j/16) + 8*((j%16)/4) + 4*g + j%4; unused positions are 0
@@ -141,6 +147,7 @@ typedef struct {
   uint64_t off_scores, off_lmax, off_rank_state, off_rank_hist;
   uint64_t off_map, off_lists, off_counts, off_out, off_zeros, off_order;
   uint64_t off_stage;
+  uint64_t off_q_nv_scale, off_k_nv_scale, off_q_nv_bf16, off_k_nv_bf16, off_nv_tscale, off_qk_amax;
   uint64_t total_bytes;
 } dap_layout;
 
@@ -153,9 +160,14 @@ dap_status dap_workspace_bytes(const dap_config* cfg, size_t* bytes);
 /* Pure host.  Fills *out with derived sizes and section offsets (see dap_layout). */
 dap_status dap_workspace_layout(const dap_config* cfg, dap_layout* out);
 
-/* Region reorder + pad, avg/max pooling, INT8 / MXFP4 quantisation of Q and K, V reorder,
- * transpose and pack (bf16 and FP8).  q, k, v: device bf16 [batch, heads, N, D]; read only.
- * Formats of a precision whose quota is 0 are not written. */
+/* Region reorder + pad, avg/max pooling, INT8 and 4-bit (MXFP4, or NVFP4 per fp4_format)
+ * quantisation of Q and K, V reorder, transpose and pack (bf16 and FP8).  q, k, v: device bf16
+ * [batch, heads, N, D]; read only.  Formats of a precision whose quota is 0 are not written.
+ * NVFP4 (pchao.org blog, section 方法概览 bullet 2, the pages' example 4-bit format): one fp32
+ * tensor scale t = amax/2688 per (batch, head, tensor), E4M3 scales per 16 channels
+ * s = E4M3(a_16 / 6t), codes E2M1(|x| x 1/(s t)), every step in fp32; the 4-bit Q K^T then runs
+ * on the exactly dequantised bf16 values E2M1 x s and applies t_q t_k with the softmax scale
+ * (gfx950's scaled matrix-core instructions take power-of-two scales per 32 channels only). */
 dap_status dap_prepare(const dap_config* cfg, const void* q, const void* k, const void* v,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 

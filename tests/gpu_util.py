@@ -76,6 +76,14 @@ class Sections:
         self.lists = sec("lists", torch.int16, (BH, Nb, Nb)).view(np.uint16)
         self.counts = sec("counts", torch.int32, (BH, Nb, 4))
         self.out_packed = sec("out", torch.int16, (BH, Np, D)).view(np.uint16)
+        # NVFP4 sections exist only when the layout gives them room
+        self.nv = L["off_q_nv_bf16"] != L["off_k_nv_bf16"]
+        if self.nv:
+            self.q_nv_s = sec("q_nv_scale", torch.uint8, (BH, Np, D // 16))
+            self.k_nv_s = sec("k_nv_scale", torch.uint8, (BH, Np, D // 16))
+            self.q_nv_bf16 = sec("q_nv_bf16", torch.int16, (BH, Np, D)).view(np.uint16)
+            self.k_nv_bf16 = sec("k_nv_bf16", torch.int16, (BH, Np, D)).view(np.uint16)
+            self.nv_t = sec("nv_tscale", torch.float32, (BH, 2))
         # sections of a precision no pair uses are never written: decode only the used ones
         need16 = L["c16"] > 0
         needlow = L["c4"] > L["c16"]

@@ -43,7 +43,7 @@ def _attend_blocks(args):
     the given query blocks.  Returns (packed rows, fp64 outputs of those rows)."""
     from oracle import pipeline as opipe
     q, k, v, geo, blocks = args
-    r = opipe.prepare_head(q, k, v, **geo)
+    r = opipe.prepare_head(q, k, v, **geo)  # geo may carry fp4_format
     opipe.attend(r, q_blocks=blocks)
     rows = np.concatenate([qb * r.B + np.flatnonzero(r.valid[qb]) for qb in blocks])
     return rows, r.out_packed[rows]

@@ -117,6 +117,10 @@ def _layout_py(w):
              ("rank_state", bh * 3 * 32), ("rank_hist", bh * 3 * 2048 * 4), ("map", bh * Nb * Nb),
              ("lists", bh * Nb * Nb * 2), ("counts", bh * Nb * 16), ("out", bh * Np * D * 2),
              ("zeros", 256), ("order", 8 * bh * -(-Nb // 8) * 4), ("stage", 8)]
+    nv = 1 if getattr(w, "fp4", "mxfp4") == "nvfp4" else 0  # NVFP4 sections, empty for MXFP4
+    sizes += [("q_nv_scale", nv * bh * Np * D // 16), ("k_nv_scale", nv * bh * Np * D // 16),
+              ("q_nv_bf16", nv * bh * Np * D * 2), ("k_nv_bf16", nv * bh * Np * D * 2),
+              ("nv_tscale", nv * bh * 8), ("qk_amax", nv * 2 * bh * D * 4)]
     off, o = {}, 0
     for name, n in sizes:
         off["off_" + name] = o
@@ -128,9 +132,10 @@ def _layout_py(w):
                 Wp=nbx * w.region_w, pairs=P, c16=rnd(q16), c8=rnd(q16 + q8), c4=rnd(q16 + q8 + q4))
 
 
+@pytest.mark.parametrize("fp4", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
-def test_workspace_layout_matches_rederivation(name):
-    w = synth.WORKLOADS[name]
+def test_workspace_layout_matches_rederivation(name, fp4):
+    w = synth.WORKLOADS[name].with_(fp4=fp4)
     L = b.workspace_layout(b.Config.from_workload(w))
     exp = _layout_py(w)
     for k, v in exp.items():

@@ -39,7 +39,16 @@ def _inputs(w, exact_heads=None):
 def _oracle_head(w, Q, K, V, bhi):
     bb, h = divmod(bhi, w.heads)
     return opipe.prepare_head(Q[bb, h], K[bb, h], V[bb, h], T=w.T, H=w.H, W=w.W, rh=w.region_h,
-                              rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp)
+                              rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp, fp4_format=w.fp4)
+
+
+def _nv_value_bits(codes, scale_bytes):
+    """bf16 bits of E2M1 value x E4M3 group scale with the code's sign (exact in bf16)."""
+    from oracle import quant
+    c = codes.astype(np.int64)
+    mag = quant.E2M1_GRID[c & 7] * np.repeat(quant.e4m3fn_decode(scale_bytes), 16, axis=-1)
+    bits = (mag.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return bits | ((c & 8) << 12).astype(np.uint16)
 
 
 def _check_prep(S: Sections, r, L):
@@ -57,7 +66,16 @@ def _check_prep(S: Sections, r, L):
         np.testing.assert_array_equal(S.k_i8, r.k_i8, err_msg="k int8")
         np.testing.assert_array_equal(S.q_i8_s.view(np.uint32), r.q_i8_s.view(np.uint32))
         np.testing.assert_array_equal(S.k_i8_s.view(np.uint32), r.k_i8_s.view(np.uint32))
-    if need4:
+    if need4 and r.fp4_format == "nvfp4":
+        assert S.nv
+        for name, got_c, got_s, got_b, t_idx, rc, rs, rt in (
+                ("q", S.q_fp4, S.q_nv_s, S.q_nv_bf16, 0, r.q_nv, r.q_nv_s, r.q_nv_t),
+                ("k", S.k_fp4, S.k_nv_s, S.k_nv_bf16, 1, r.k_nv, r.k_nv_s, r.k_nv_t)):
+            np.testing.assert_array_equal(got_c, rc, err_msg=f"{name} nvfp4 codes")
+            np.testing.assert_array_equal(got_s, rs, err_msg=f"{name} nvfp4 e4m3 scales")
+            assert S.nv_t[t_idx].view(np.uint32) == np.float32(rt).view(np.uint32), f"{name} tensor scale"
+            np.testing.assert_array_equal(got_b, _nv_value_bits(rc, rs), err_msg=f"{name} nvfp4 bf16")
+    elif need4:
         np.testing.assert_array_equal(S.q_fp4, r.q_fp4, err_msg="q mxfp4 codes")
         np.testing.assert_array_equal(S.k_fp4, r.k_fp4, err_msg="k mxfp4 codes")
         np.testing.assert_array_equal(S.q_e8, r.q_e8, err_msg="q e8m0")
@@ -142,7 +160,8 @@ def _sample_blocks(r, S, k=12, seed=0):
 
 
 def _geo_kw(w):
-    return dict(T=w.T, H=w.H, W=w.W, rh=w.region_h, rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp)
+    return dict(T=w.T, H=w.H, W=w.W, rh=w.region_h, rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp,
+                fp4_format=w.fp4)
 
 
 def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None, inputs=None,
@@ -150,7 +169,7 @@ def _run_case(w, exact_heads=None, sample_blocks=None, check_heads=None, inputs=
     """`sample_blocks`: compare that many sampled query blocks per checked head (None: all);
     heads in `all_blocks_heads` are compared over every query block, with the oracle's attention
     split over the worker pool."""
-    log(f"case {w.name} quota={w.quota_bp} lam={w.lam} batch={w.batch}")
+    log(f"case {w.name} quota={w.quota_bp} lam={w.lam} batch={w.batch} fp4={w.fp4}")
     Q, K, V = _inputs(w, exact_heads) if inputs is None else inputs
     cfg = b.Config.from_workload(w)
     q, k, v = to_device(Q, K, V)
@@ -458,3 +477,37 @@ def test_parity_full_size_one_head_every_block():
     w = synth.workload(2)
     _run_case(w, exact_heads=[0, w.heads - 1], sample_blocks=10, check_heads=[0, w.heads - 1],
               all_blocks_heads=(0,))
+
+
+# ------------------------------------------------------------------------------------ NVFP4
+# The pages' example 4-bit format (pchao.org blog, section 方法概览 bullet 2) selected instead of
+# MXFP4: codes, E4M3 group scales, tensor scales and the bf16 operands of the 4-bit Q K^T are
+# bit-exact; outputs within the usual tolerance.
+
+@pytest.mark.parametrize("quota", [(0, 10000, 0, 0), (2000, 2000, 3000, 3000), (7000, 1000, 1000, 1000)])
+@pytest.mark.parametrize("dims", [(128, 8, 16), (64, 8, 16), (128, 4, 32)])
+def test_nvfp4_block128_small(dims, quota):
+    D, rh, rw = dims
+    w = synth.Workload("b128nv", 2, 20, 36, 2, D, rh, rw, 0.5, quota, seed=4250, fp4="nvfp4")
+    _run_case(w)
+
+
+@pytest.mark.parametrize("wi,D", [(0, 64), (0, 128), (1, 64)])
+def test_nvfp4_block16_and_64(wi, D):
+    w = synth.workload(wi).with_(quota_bp=(2500, 5000, 1000, 1500), head_dim=D, heads=2, fp4="nvfp4")
+    _run_case(w)
+
+
+def test_nvfp4_zero_tensor():
+    # head 0 has Q = 0: its tensor scale is 0, every NVFP4 code and scale of Q is 0
+    w = synth.Workload("nvzero", 4, 40, 64, 2, 128, 8, 16, 0.5, (5000, 3000, 1000, 1000), seed=4251,
+                       fp4="nvfp4")
+    Q, K, V = synth.make_inputs(w)
+    Q[0, 0] = 0
+    _run_case(w, inputs=(Q, K, V))
+
+
+@pytest.mark.parametrize("wi", [3, 4])
+def test_nvfp4_full_size(wi):
+    w = synth.workload(wi).with_(fp4="nvfp4")
+    _run_case(w, exact_heads=[0, w.heads - 1], sample_blocks=10, check_heads=[0, w.heads - 1])

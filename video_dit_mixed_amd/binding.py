@@ -47,7 +47,8 @@ _LAYOUT_INT64 = ["pairs", "c16", "c8", "c4"]
 _LAYOUT_OFFS = ["q_bf16", "k_bf16", "vt_bf16", "q_i8", "k_i8", "q_i8_scale", "k_i8_scale",
                 "q_fp4", "k_fp4", "q_e8m0", "k_e8m0", "vt_fp8", "v_scale", "v_amax",
                 "q_avg", "q_max", "k_avg", "k_max", "scores", "lmax", "rank_state", "rank_hist",
-                "map", "lists", "counts", "out", "zeros", "order", "stage"]
+                "map", "lists", "counts", "out", "zeros", "order", "stage", "q_nv_scale",
+                "k_nv_scale", "q_nv_bf16", "k_nv_bf16", "nv_tscale", "qk_amax"]
 
 
 class _Layout(ctypes.Structure):
@@ -74,7 +75,8 @@ class Config:
     @classmethod
     def from_workload(cls, w, **override) -> "Config":
         kw = dict(batch=w.batch, heads=w.heads, head_dim=w.head_dim, T=w.T, H=w.H, W=w.W,
-                  region_h=w.region_h, region_w=w.region_w, lam=w.lam, quota_bp=tuple(w.quota_bp))
+                  region_h=w.region_h, region_w=w.region_w, lam=w.lam, quota_bp=tuple(w.quota_bp),
+                  fp4_format=FP4_NVFP4 if getattr(w, "fp4", "mxfp4") == "nvfp4" else FP4_MXFP4)
         kw.update(override)
         return cls(**kw)
 

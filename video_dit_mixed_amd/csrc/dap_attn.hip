@@ -63,11 +63,12 @@ struct AttnCfg {
 };
 
 // Per-phase tile geometry.  PH = 0: bf16 K rows / bf16 V^T rows; 1: int8 K / e4m3 V^T;
-// 2: E2M1 K (+ E8M0 scales) / e4m3 V^T.
+// 2: E2M1 K (+ E8M0 scales) / e4m3 V^T; 3 (4-bit level in NVFP4): bf16 rows of the dequantised
+// NVFP4 K / e4m3 V^T.
 template <int B, int D, int PH>
 struct PhaseCfg {
   using C = AttnCfg<B, D>;
-  static constexpr int KRB = PH == 0 ? 2 * D : (PH == 1 ? D : D / 2);  // key row bytes
+  static constexpr int KRB = (PH == 0 || PH == 3) ? 2 * D : (PH == 1 ? D : D / 2);  // key row bytes
   static constexpr int KRC = KRB / 16;                                 // 16-byte chunks per row
   static constexpr int VRB = PH == 0 ? 2 * B : C::KP8;                 // V^T row bytes
   static constexpr int VRC = VRB / 16;
@@ -196,6 +197,7 @@ template <int B, int D, int PH>
 __device__ __forceinline__ const uint8_t* k_tile_src(const Geo& g, const Ws& w, int bh, int kb) {
   const size_t krow0 = (size_t)bh * g.Np + (size_t)kb * B;
   return PH == 0 ? reinterpret_cast<const uint8_t*>(w.k_bf16 + krow0 * D)
+       : PH == 3 ? reinterpret_cast<const uint8_t*>(w.k_nv_bf16 + krow0 * D)
        : PH == 1 ? reinterpret_cast<const uint8_t*>(w.k_i8 + krow0 * D)
                  : w.k_fp4 + krow0 * (D / 2);
 }
@@ -220,7 +222,8 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
   // Q operand for this phase, straight from the packed workspace
-  constexpr int NQ = PH == 0 ? D / 16 : (PH == 1 ? D / 32 : D / 64);
+  constexpr bool kQk16 = PH == 0 || PH == 3;  // bf16 Q K^T (16-bit level, NVFP4 4-bit level)
+  constexpr int NQ = kQk16 ? D / 16 : (PH == 1 ? D / 32 : D / 64);
   uint4 qop[NQ];
   int qsc[NQ];
   float s_q = 0.0f;
@@ -228,12 +231,18 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
   for (int ks = 0; ks < NQ; ++ks) {
     const uint8_t* base =
         PH == 0 ? reinterpret_cast<const uint8_t*>(w.q_bf16 + c.qrow * D) + 32 * ks + 16 * gh
+        : PH == 3 ? reinterpret_cast<const uint8_t*>(w.q_nv_bf16 + c.qrow * D) + 32 * ks + 16 * gh
         : PH == 1 ? reinterpret_cast<const uint8_t*>(w.q_i8 + c.qrow * D) + 32 * ks + 16 * gh
                   : w.q_fp4 + c.qrow * (D / 2) + 32 * ks + 16 * gh;
     qop[ks] = c.qok ? *reinterpret_cast<const uint4*>(base) : make_uint4(0, 0, 0, 0);
     qsc[ks] = (PH == 2 && c.qok) ? (int)w.q_e8m0[c.qrow * (D / 32) + 2 * ks + gh] : 127;
   }
   if (PH == 1) s_q = __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(w.q_i8_scale) + (size_t)c.bh * g.Nb + c.qb));
+  float nv_t = 0.0f;  // NVFP4: product of the Q and K tensor scales of this head
+  if (PH == 3) {
+    const uint32_t* ts = reinterpret_cast<const uint32_t*>(w.nv_tscale) + (size_t)c.bh * 2;
+    nv_t = __uint_as_float(uniform_load(ts)) * __uint_as_float(uniform_load(ts + 1));
+  }
   using P = PhaseCfg<B, D, PH>;
   const int lane = c.tid & 63;
   TileMover<C::KT, P::KRC, C::NT, C::DIRECT> kt;
@@ -305,10 +314,12 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     if (PH == 1)
       c_scale = s_q * sk *
                 (kLog2e * inv_sqrt_d);
+    if (PH == 3)  // NVFP4: the operands carry the group scales, the tensor scales apply here
+      c_scale = nv_t * (kLog2e * inv_sqrt_d);
     f32x16 S[C::MT];  // the 8-bit phase keeps its int32 sums here (bit patterns) until converted
     float mx = -INFINITY;
     auto qk_tile = [&](int mt) {
-      if (PH == 0) {
+      if (kQk16) {
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks)
@@ -346,7 +357,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[mt][r] = (float)si[r];
       }
-      if (kFull || (PH == 0 && full)) {
+      if (kFull || (kQk16 && full)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[mt][r]);
       } else {
@@ -380,7 +391,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     // is straight-line code in which the scheduler can interleave products, conversions and
     // maxima.  The 16-bit phase keeps the choice per m-tile: two copies of it do not fit in the
     // registers.
-    if (PH != 0 && full)
+    if (!kQk16 && full)
       qk_all(std::true_type{});
     else
       qk_all(std::false_type{});
@@ -481,7 +492,9 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
   }
 }
 
-template <int B, int D>
+// kNv: the 4-bit level runs in NVFP4 (phase 3) instead of MXFP4 (phase 2); a separate
+// instantiation, so that each kernel holds the registers of its own phases only
+template <int B, int D, bool kNv>
 __global__ __launch_bounds__(64 * (B >= 32 ? B / 32 : 1)) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_kernel(Geo g, Ws w) {
   using C = AttnCfg<B, D>;
@@ -563,7 +576,7 @@ void attn_kernel(Geo g, Ws w) {
       }
   }
   if (n8 > 0) run_phase<B, D, 1>(g, w, c, O, m_run, l_run, n8, n16, sK, sV, sKs, sBias);
-  if (n4 > 0) run_phase<B, D, 2>(g, w, c, O, m_run, l_run, n4, n16 + n8, sK, sV, sKs, sBias);
+  if (n4 > 0) run_phase<B, D, kNv ? 3 : 2>(g, w, c, O, m_run, l_run, n4, n16 + n8, sK, sV, sKs, sBias);
 
   // ---- finalise: O / l (0 when no pair was kept), undo the low-bit units, bf16 out
   const float l = halves_sum(l_run);
@@ -598,7 +611,11 @@ void attn_kernel(Geo g, Ws w) {
 template <int B, int D>
 hipError_t attn_bd(const Geo& g, const Ws& w, hipStream_t s) {
   using C = AttnCfg<B, D>;
-  attn_kernel<B, D><<<(unsigned)(kXcds * xcd_stride(g.bh, g.Nb)), C::NT, 0, s>>>(g, w);
+  const unsigned grid = (unsigned)(kXcds * xcd_stride(g.bh, g.Nb));
+  if (g.fp4_format == DAP_FP4_NVFP4)
+    attn_kernel<B, D, true><<<grid, C::NT, 0, s>>>(g, w);
+  else
+    attn_kernel<B, D, false><<<grid, C::NT, 0, s>>>(g, w);
   return hipGetLastError();
 }
 

@@ -26,7 +26,6 @@ dap_status validate(const dap_config* c) {
   }
   if (qsum > 10000) return DAP_E_INVALID;
   if (c->fp4_format != DAP_FP4_MXFP4 && c->fp4_format != DAP_FP4_NVFP4) return DAP_E_INVALID;
-  if (c->fp4_format != DAP_FP4_MXFP4) return DAP_E_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return DAP_E_UNSUPPORTED;
   const long long B = (long long)c->region_h * c->region_w;
   if (B != 16 && B != 64 && B != 128) return DAP_E_UNSUPPORTED;
@@ -143,6 +142,13 @@ void make_layout(const Geo& g, dap_layout* L) {
   L->off_zeros = take(256);
   L->off_order = take((uint64_t)dap::kXcds * dap::xcd_stride(g.bh, g.Nb) * 4);
   L->off_stage = take(8);
+  const uint64_t nv = g.fp4_format == DAP_FP4_NVFP4 ? 1 : 0;  // NVFP4 sections, empty otherwise
+  L->off_q_nv_scale = take(nv * bh * Np * D / 16);
+  L->off_k_nv_scale = take(nv * bh * Np * D / 16);
+  L->off_q_nv_bf16 = take(nv * bh * Np * D * 2);
+  L->off_k_nv_bf16 = take(nv * bh * Np * D * 2);
+  L->off_nv_tscale = take(nv * bh * 2 * 4);
+  L->off_qk_amax = take(nv * 2 * bh * D * 4);
   L->total_bytes = o;
 }
 
@@ -178,6 +184,12 @@ Ws make_ws(void* base, const dap_layout& L) {
   w.zeros = reinterpret_cast<uint8_t*>(b + L.off_zeros);
   w.order = reinterpret_cast<uint32_t*>(b + L.off_order);
   w.stage = reinterpret_cast<uint32_t*>(b + L.off_stage);
+  w.q_nv_scale = reinterpret_cast<uint8_t*>(b + L.off_q_nv_scale);
+  w.k_nv_scale = reinterpret_cast<uint8_t*>(b + L.off_k_nv_scale);
+  w.q_nv_bf16 = reinterpret_cast<uint16_t*>(b + L.off_q_nv_bf16);
+  w.k_nv_bf16 = reinterpret_cast<uint16_t*>(b + L.off_k_nv_bf16);
+  w.nv_tscale = reinterpret_cast<float*>(b + L.off_nv_tscale);
+  w.qk_amax = reinterpret_cast<uint32_t*>(b + L.off_qk_amax);
   return w;
 }
 

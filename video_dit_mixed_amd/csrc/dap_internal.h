@@ -52,6 +52,12 @@ struct Ws {
   uint8_t* zeros;
   uint32_t* order;
   uint32_t* stage;  // [0] stage word (DAP_STAGE_*), [1] configuration tag
+  uint8_t* q_nv_scale;   // NVFP4 (fp4_format DAP_FP4_NVFP4): e4m3 scale per 16 channels
+  uint8_t* k_nv_scale;
+  uint16_t* q_nv_bf16;   // NVFP4 values without the tensor scale, as bf16 (exact)
+  uint16_t* k_nv_bf16;
+  float* nv_tscale;      // [bh][2]: tensor scales of Q and K
+  uint32_t* qk_amax;     // [2][bh][D]: per-channel |Q| and |K| maxima (fp32 bits)
 };
 
 // Stage words: DAP_STAGE_* = kStageMagic | stage number; `accept` masks of launch_stage are sets

@@ -19,6 +19,15 @@
 //                             code = e4m3fn rne of x*r (|x*r| <= 448, so no saturation case;
 //                             the hardware converter v_cvt_pk_fp8_f32), scale = a_d/448; a_d = 0,
 //                             or r overflowing (a_d below about 1.3e-36) -> codes 0, scale 0.
+//   NVFP4 per (head, tensor) and (row, 16 ch), when selected instead of MXFP4 (the pages'
+//                             example 4-bit format, blog section 方法概览 bullet 2):
+//                             t = amax/2688 over the head's tensor (per-channel maxima from
+//                             v_amax_kernel, then their maximum), d = 6 t, scale byte =
+//                             e4m3fn rne of a_16 / d (hardware converter), step = scale x t,
+//                             inv = 1/step (0 if step is 0 or inv overflows), code = E2M1 of
+//                             |x| x inv with the sign bit of x; t = 0 -> every code and scale 0.
+//                             Also written: E2M1 value x scale as bf16 (exact: at most 6
+//                             significant bits), the operand of the 4-bit Q K^T.
 // Launch shapes: prep_qk one 256-thread workgroup per (block, head, tensor); v_amax a grid of
 // token slices per head; v_pack one workgroup per (block, head).  Reads are whole region rows
 // (region_w * D * 2 contiguous bytes) with 16-byte lanes.
@@ -64,6 +73,17 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   if (amax == 0.0f || ef == 0) return -127;  // zero or subnormal: floor(log2) - 2 < -127
   int e = (int)ef - 127 - 2;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Value of a non-negative finite e4m3fn code (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e == 0 ? (float)m * 0.001953125f : ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// Value of an E2M1 magnitude code 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_value(uint32_t m) {
+  return m < 4u ? 0.5f * (float)m : (m == 7u ? 6.0f : (float)m - 2.0f);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -219,8 +239,62 @@ __global__ __launch_bounds__(kThreads) void prep_qk_kernel(Geo g, const uint16_t
     }
   }
 
+  // NVFP4 per (row, 16-channel group): a group is 2 adjacent lanes (chunks 2G, 2G+1)
+  if (g.need4 && g.fp4_format == DAP_FP4_NVFP4) {
+    float ta = 0.0f;  // the head's tensor maximum: maximum of the per-channel maxima
+    for (int ch = tid; ch < D; ch += kThreads)
+      ta = fmaxf(ta, __uint_as_float(w.qk_amax[((size_t)tensor * g.bh + bh) * D + ch]));
+    ta = wave_max(ta);
+    __syncthreads();  // every thread has read s_red for the block maximum
+    if ((tid & 63) == 0) s_red[tid >> 6] = ta;
+    __syncthreads();
+    ta = s_red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) ta = fmaxf(ta, s_red[i]);
+    const float t = ta / 2688.0f;
+    if (b == 0 && tid == 0) w.nv_tscale[(size_t)bh * 2 + tensor] = t;
+    const float d6 = 6.0f * t;
+    uint8_t* dst = tensor == 0 ? w.q_fp4 : w.k_fp4;
+    uint8_t* dsc = tensor == 0 ? w.q_nv_scale : w.k_nv_scale;
+    uint16_t* dbf = tensor == 0 ? w.q_nv_bf16 : w.k_nv_bf16;
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+      float x[8];
+      unpack8(raw[p], x);
+      float ga = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ga = fmaxf(ga, fabsf(x[j]));
+      ga = fmaxf(ga, __shfl_xor(ga, 1));
+      if (!inblk[p]) continue;
+      uint32_t sgc = 0;
+      float sgv = 0.0f, inv = 0.0f;
+      if (t > 0.0f) {
+        // e4m3fn, round to nearest even: a_16 / d <= 448 (1 + 2^-23), so never past 448
+        sgc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ga / d6, 0.0f, 0, false) & 0xffu;
+        sgv = e4m3_value(sgc);
+        const float step = sgv * t;
+        inv = step > 0.0f ? 1.0f / step : 0.0f;
+        if (!(inv <= 3.402823466e38f)) inv = 0.0f;
+      }
+      uint32_t packed = 0;
+      uint32_t bw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sgn = t > 0.0f ? (word_of(raw[p], j >> 1) >> ((j & 1) ? 31 : 15)) & 1u : 0u;
+        const uint32_t mag = e2m1_code(fabsf(x[j]) * inv);
+        packed |= (mag | (sgn << 3)) << (4 * j);
+        const uint32_t vb = (__float_as_uint(e2m1_value(mag) * sgv) >> 16) | (sgn << 15);
+        bw[j >> 1] |= vb << (16 * (j & 1));
+      }
+      const size_t row = row0 + r0 + p * RP;
+      *reinterpret_cast<uint32_t*>(dst + row * (D / 2) + c * 4) = packed;
+      *reinterpret_cast<uint4*>(dbf + row * D + c * 8) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+      if ((c & 1) == 0) dsc[row * (D / 16) + (c >> 1)] = (uint8_t)sgc;
+    }
+  }
+
   // MXFP4 per (row, 32-channel group): a group is 4 adjacent lanes (chunks 4G..4G+3)
-  if (g.need4) {
+  if (g.need4 && g.fp4_format == DAP_FP4_MXFP4) {
     uint8_t* dst = tensor == 0 ? w.q_fp4 : w.k_fp4;
     uint8_t* dse = tensor == 0 ? w.q_e8m0 : w.k_e8m0;
 #pragma unroll
@@ -419,12 +493,18 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 template <int D>
 hipError_t prepare_d(const Geo& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const Ws& w, hipStream_t s) {
-  prep_qk_kernel<D><<<dim3(g.Nb, g.bh, 2), kThreads, 0, s>>>(g, q, k, w);
-  const size_t na = (size_t)g.bh * D;
-  fill_u32_kernel<<<(unsigned)((na + 255) / 256), 256, 0, s>>>(w.v_amax, na, 0u);
-  fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t*>(w.zeros), 64, 0u);
   const int slice = 2048;
   const int slices = (g.N + slice - 1) / slice;
+  const size_t na = (size_t)g.bh * D;
+  if (g.need4 && g.fp4_format == DAP_FP4_NVFP4) {
+    // per-channel maxima of |Q| and |K| for the NVFP4 tensor scales
+    fill_u32_kernel<<<(unsigned)((2 * na + 255) / 256), 256, 0, s>>>(w.qk_amax, 2 * na, 0u);
+    v_amax_kernel<D><<<dim3(slices, g.bh), kThreads, 0, s>>>(g, q, w.qk_amax, slice);
+    v_amax_kernel<D><<<dim3(slices, g.bh), kThreads, 0, s>>>(g, k, w.qk_amax + na, slice);
+  }
+  prep_qk_kernel<D><<<dim3(g.Nb, g.bh, 2), kThreads, 0, s>>>(g, q, k, w);
+  fill_u32_kernel<<<(unsigned)((na + 255) / 256), 256, 0, s>>>(w.v_amax, na, 0u);
+  fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t*>(w.zeros), 64, 0u);
   v_amax_kernel<D><<<dim3(slices, g.bh), kThreads, 0, s>>>(g, v, w.v_amax, slice);
   v_pack_kernel<D><<<dim3(g.Nb, g.bh), kThreads, 0, s>>>(g, v, w);
   return hipGetLastError();

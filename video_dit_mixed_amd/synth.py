@@ -46,6 +46,7 @@ class Workload:
     quota_bp: Tuple[int, int, int, int]
     batch: int = 1
     seed: int = 0
+    fp4: str = "mxfp4"   # 4-bit operand format of the workload: "mxfp4" or "nvfp4"
 
     @property
     def N(self) -> int:
