@@ -88,9 +88,10 @@ class _Ops:
 
 
 def prepare_head(q_bits, k_bits, v_bits, *, T, H, W, rh, rw, lam, quota_bp,
-                 levels_override=None, fp4_format: str = "mxfp4") -> HeadResult:
+                 levels_override=None, fp4_format: str = "mxfp4", mx_rule: str = "ocp") -> HeadResult:
     """Every step up to (not including) attention for one head.  q/k/v_bits: [N, D] bf16 bits.
-    fp4_format: the 4-bit level's operands, OCP MXFP4 (R17) or NVFP4 (R30)."""
+    fp4_format: the 4-bit level's operands, OCP MXFP4 (R17) or NVFP4 (R30); mx_rule: MXFP4's
+    scale rule (see quant.mxfp4; the path implements "ocp", "ceil" is compared in the sweep)."""
     g = layout.geometry(T, H, W, rh, rw)
     q = bf16_bits_to_f64(q_bits)
     k = bf16_bits_to_f64(k_bits)
@@ -115,8 +116,8 @@ def prepare_head(q_bits, k_bits, v_bits, *, T, H, W, rh, rw, lam, quota_bp,
         s = slice(b * B, (b + 1) * B)
         q_i8[s], q_i8_s[b] = quant.int8_block(qp[s])
         k_i8[s], k_i8_s[b] = quant.int8_block(kp[s])
-    q_fp4, q_e8 = quant.mxfp4(qp)
-    k_fp4, k_e8 = quant.mxfp4(kp)
+    q_fp4, q_e8 = quant.mxfp4(qp, rule=mx_rule)
+    k_fp4, k_e8 = quant.mxfp4(kp, rule=mx_rule)
     v_fp8, v_s = quant.fp8_v(v, vp)
 
     r = HeadResult(g, D, B, valid, qp, kp, vp, q_avg, q_max, k_avg, k_max, A, A_avg, A_max,

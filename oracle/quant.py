@@ -140,17 +140,28 @@ def int8_block(x: np.ndarray):
 # MXFP4 per (row, 32-channel group)
 
 
-def mxfp4(x: np.ndarray):
+def mxfp4(x: np.ndarray, rule: str = "ocp"):
     """MXFP4 of rows x [..., D] (fp64 values of bf16), groups of 32 consecutive channels.
 
     Returns (codes uint8 [..., D] in 0..15 with bit 3 = sign, e8m0 uint8 [..., D/32]).
-    e = clamp(floor(log2 amax) - 2, -127, 127), amax = 0 gives -127; byte = e + 127.
+    rule "ocp" (R17, the path's rule): e = floor(log2 amax) - 2, so amax 2^-e lies in [4, 8) and
+      the top of that binade saturates at 6.
+    rule "ceil" (R17's listed alternative, compared in the quality sweep only): the smallest e with
+      amax <= 6 * 2^e, i.e. ceil(log2(amax / 6)): nothing saturates, amax 2^-e lies in (3, 6].
+    Either way e is clamped to [-127, 127], amax = 0 gives -127; byte = e + 127.
     code = E2M1_rne_sat(x * 2^-e) with the sign bit of x."""
     x = np.asarray(x, dtype=np.float64)
     D = x.shape[-1]
     xg = x.reshape(x.shape[:-1] + (D // 32, 32))
     a = np.max(np.abs(xg), axis=-1)
-    e = np.where(a > 0, _floor_log2(np.where(a > 0, a, 1.0)) - 2, -127)
+    fl = _floor_log2(np.where(a > 0, a, 1.0))
+    if rule == "ocp":
+        e = np.where(a > 0, fl - 2, -127)
+    elif rule == "ceil":
+        # log2(a / 6) lies in [fl - 2.59, fl - 1.59): the answer is fl - 2 when a <= 6 * 2^(fl - 2)
+        e = np.where(a > 0, np.where(a <= 6.0 * np.ldexp(1.0, fl - 2), fl - 2, fl - 1), -127)
+    else:
+        raise ValueError(rule)
     e = np.clip(e, -127, 127)
     scaled = xg * np.ldexp(1.0, -e)[..., None]
     mag = e2m1_rne_sat(scaled)

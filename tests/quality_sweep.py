@@ -15,8 +15,11 @@ a 4-bit pair 1/10.1 + 1/5).
   gpu leg  the HIP path through the C ABI at a full-size layer; the error is taken on a sample of
            query rows of several heads, against the oracle's exact dense rows (fp64).
   cpu leg  the oracle alone (phased attention with its emulated roundings) on a reduced layer with
-           the same block geometry, against exact dense attention over every row; --fp4 nvfp4
-           swaps the 4-bit level's MXFP4 Q/K for NVFP4 (the pages' example format) to compare.
+           the same block geometry, against exact dense attention over every row.
+  --fp4 nvfp4 runs the 4-bit level in NVFP4 (the pages' example format) instead of MXFP4, on
+           either leg (the GPU leg then takes only the allocations that have 4-bit pairs);
+  --mx-rule ceil (cpu leg) takes MXFP4's alternative scale rule e = ceil(log2(amax/6)), which
+           never saturates, instead of the OCP rule floor(log2 amax) - 2 the path implements.
 
 rel-L2 = ||O - O_dense||_2 / ||O_dense||_2 over the rows taken; the bf16 rounding of the output
 alone gives about 1.1e-3.
@@ -88,7 +91,7 @@ def gpu_leg(args):
     from video_dit_mixed_amd import binding as b
     if not torch.cuda.is_available():
         sys.exit("the gpu leg needs a GPU")
-    w = synth.workload(args.workload)
+    w = synth.workload(args.workload).with_(fp4=args.fp4)
     heads_total = w.batch * w.heads
     pick = np.linspace(0, heads_total - 1, args.heads).round().astype(int)
     rng = np.random.default_rng(args.seed)
@@ -111,6 +114,8 @@ def gpu_leg(args):
     stream = torch.cuda.current_stream()
     results = []
     for name, quota, lam in allocations():
+        if args.fp4 == "nvfp4" and quota[1] == 0:
+            continue  # no 4-bit pair: the same result as with MXFP4
         cfg = b.Config.from_workload(w, quota_bp=tuple(quota), lam=lam)
         ws = b.alloc_workspace(cfg, dev)
         b.forward(cfg, q, k, v, ws, out)
@@ -134,7 +139,7 @@ def gpu_leg(args):
         r2, mabs = rel(np.concatenate(got), np.concatenate(exp))
         del ws
         torch.cuda.empty_cache()
-        r = {"leg": "gpu", "workload": w.name, "allocation": name,
+        r = {"leg": "gpu", "fp4": args.fp4, "workload": w.name, "allocation": name,
              "quota_bp_skip_4_8_16": list(quota), "lambda": lam,
              "t_roof_units_per_bp": round(budget(quota), 2),
              "attention_ms_median": round(statistics.median(times), 3),
@@ -147,7 +152,7 @@ def gpu_leg(args):
 
 
 def cpu_leg(args):
-    from oracle import pipeline, quant
+    from oracle import pipeline
     # same 8x16-region, 128-token block geometry as the full-size layers, smaller latent
     w = synth.Workload("quality_small_4x24x48", 4, 24, 48, 2, 128, 8, 16, 0.5,
                        (8500, 0, 750, 750), seed=2024)
@@ -158,20 +163,20 @@ def cpu_leg(args):
         ref[bh] = odense.dense_attention_rows(Q[b_, h_], K[b_, h_], V[b_, h_])
     results = []
     for name, quota, lam in allocations():
+        if (args.fp4 == "nvfp4" or args.mx_rule != "ocp") and quota[1] == 0:
+            continue  # no 4-bit pair: the same result as the default leg
         t0 = time.perf_counter()
         got, exp = [], []
         for bh in range(w.batch * w.heads):
             b_, h_ = divmod(bh, w.heads)
             r = pipeline.prepare_head(Q[b_, h_], K[b_, h_], V[b_, h_], T=w.T, H=w.H, W=w.W,
-                                      rh=w.region_h, rw=w.region_w, lam=lam, quota_bp=tuple(quota))
-            if args.fp4 == "nvfp4":
-                # the pages' 4-bit example format in place of MXFP4 (same map, same other levels)
-                r.q_fp4_val = quant.nvfp4_dequant(r.qp)
-                r.k_fp4_val = quant.nvfp4_dequant(r.kp)
+                                      rh=w.region_h, rw=w.region_w, lam=lam, quota_bp=tuple(quota),
+                                      fp4_format=args.fp4, mx_rule=args.mx_rule)
             got.append(pipeline.attend(r).out_bf16())
             exp.append(ref[bh])
         r2, mabs = rel(np.concatenate(got), np.concatenate(exp))
-        r = {"leg": "cpu-oracle", "fp4": args.fp4, "workload": w.name, "allocation": name,
+        r = {"leg": "cpu-oracle", "fp4": args.fp4, "mx_rule": args.mx_rule,
+             "workload": w.name, "allocation": name,
              "quota_bp_skip_4_8_16": list(quota), "lambda": lam,
              "t_roof_units_per_bp": round(budget(quota), 2), "rel_l2": round(r2, 5),
              "max_abs": round(mabs, 4), "oracle_s": round(time.perf_counter() - t0, 1)}
@@ -190,7 +195,9 @@ def main():
     ap.add_argument("--seed", type=int, default=77)
     ap.add_argument("--out", default=None)
     ap.add_argument("--fp4", choices=["mxfp4", "nvfp4"], default="mxfp4",
-                    help="cpu leg: the 4-bit format of Q and K (the GPU path implements MXFP4)")
+                    help="the 4-bit format of Q and K")
+    ap.add_argument("--mx-rule", choices=["ocp", "ceil"], default="ocp",
+                    help="cpu leg: MXFP4's scale rule (the path implements ocp)")
     args = ap.parse_args()
     res = gpu_leg(args) if args.leg == "gpu" else cpu_leg(args)
     if args.out:

@@ -357,3 +357,22 @@ def test_nvfp4_exact_on_representable_values_and_zero_tensor():
     codes, sg_code, tt = quant.nvfp4(y)
     i = np.unravel_index(np.argmax(np.abs(y)), y.shape)
     assert codes[i] & 7 == 7 and quant.e4m3fn_decode(sg_code[i[0], i[1] // 16]) == 448.0
+
+
+def test_mxfp4_ceil_rule_is_the_smallest_unsaturated_exponent():
+    # the quality sweep's alternative MX scale rule: amax 2^-e in (3, 6], i.e. e = ceil(log2(amax/6)),
+    # checked against exact rational arithmetic on every finite positive bf16 group maximum
+    vals = _all_finite_bf16()
+    vals = vals[(vals > 2.0 ** -120) & (vals < 2.0 ** 120)]
+    x = np.zeros((vals.size, 32))
+    x[:, 3] = vals
+    x[:, 7] = -vals / 3
+    _, e8 = quant.mxfp4(x, rule="ceil")
+    e = e8[:, 0].astype(np.int64) - 127
+    for a, k in zip(vals[::97], e[::97]):
+        fa = Fraction(float(a))
+        assert fa <= 6 * Fraction(2) ** int(k) and fa > 6 * Fraction(2) ** (int(k) - 1), (a, k)
+    # the "ocp" rule puts the maximum in [4, 8) instead
+    _, e8o = quant.mxfp4(x, rule="ocp")
+    scaled = vals * np.ldexp(1.0, -(e8o[:, 0].astype(np.int64) - 127))
+    assert np.all((scaled >= 4) & (scaled < 8))
