@@ -13,6 +13,8 @@ The --sweep mode measures every workload (all five by default), one JSON line pe
     each precision's MFMA utilisation is seen alone;
   * the dense baseline (no skipped pair, all 16-bit) for 128-token blocks, and the speedup of the
     workload's own quota over it, per attention call and per layer.
+With --fp4 nvfp4 the 4-bit level runs in NVFP4: the sweep then takes only the workloads with 4-bit
+pairs, their own quota and the 4-bit isolated map.
 
 A step is one pass of the whole path over one batch of synthetic input, inputs resident in HBM:
 dap_prepare -> dap_draft_rank -> dap_attention -> dap_restore.  Prints one JSON line:
@@ -21,7 +23,7 @@ dap_prepare -> dap_draft_rank -> dap_attention -> dap_restore.  Prints one JSON 
                 flops per launch (4*B^2*D per kept block pair) over its average duration from
                 HIP events on the launch stream; peak = flops / T_roof with T_roof the time every
                 kept pair would take at the dense peak of its own precisions (bf16 2.5 PF/s;
-                int8 and fp8 5.0 P/s; fp4 10.1 PF/s)
+                int8 and fp8 5.0 P/s; fp4 10.1 PF/s; NVFP4's Q.K^T, run as exact bf16, at 2.5)
   cpu_baseline  the CPU oracle on a bounded sample of the same workload (a process pool over heads,
                 one worker per core), extrapolated to a layer
 """
@@ -46,8 +48,10 @@ DEFAULT_WORKLOAD = "hunyuan720p_33x45x80"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_hbm_traffic.txt")
 
 
-def roofline_terms(L: dict, heads_total: int, D: int):
-    """(algorithmic flops, T_roof seconds) of the attention kernel for one layer."""
+def roofline_terms(L: dict, heads_total: int, D: int, fp4: str = "mxfp4"):
+    """(algorithmic flops, T_roof seconds) of the attention kernel for one layer.  NVFP4's Q.K^T
+    is priced at the bf16 peak: its E4M3 group scales are not powers of two, so the scaled fp4
+    MFMA (E8M0 scales only) cannot take them and the kernel contracts the exact bf16 values."""
     B = L["B"]
     n16 = L["c16"]
     n8 = L["c8"] - L["c16"]
@@ -56,7 +60,8 @@ def roofline_terms(L: dict, heads_total: int, D: int):
     flops = heads_total * (n16 + n8 + n4) * 2 * half
     t_roof = heads_total * (n16 * (2 * half / PEAK["bf16"]) +
                             n8 * (half / PEAK["i8"] + half / PEAK["fp8"]) +
-                            n4 * (half / PEAK["fp4"] + half / PEAK["fp8"]))
+                            n4 * (half / PEAK["bf16" if fp4 == "nvfp4" else "fp4"] +
+                                  half / PEAK["fp8"]))
     return flops, t_roof, (n16, n8, n4)
 
 
@@ -304,13 +309,13 @@ def measure_case(b, w, quota, q, k, v, dev, warmup, reps, stream, label):
     del ws, out
     torch.cuda.empty_cache()
     heads = w.batch * w.heads
-    flops, t_roof, (n16, n8, n4) = roofline_terms(L, heads, w.head_dim)
+    flops, t_roof, (n16, n8, n4) = roofline_terms(L, heads, w.head_dim, w.fp4)
     med = {n: statistics.median(x) for n, x in per.items()}
     mn = {n: min(x) for n, x in per.items()}
     prep_b, rest_b, dflops, sbytes = algorithmic_bytes(L, w)
     real = (w.N / L["Np"]) ** 2
     t_attn = med["attention"] * 1e-3
-    r = {"case": label, "workload": w.name, "quota_bp_skip_4_8_16": list(quota), "reps": reps,
+    r = {"case": label, "workload": w.name, "fp4": w.fp4, "quota_bp_skip_4_8_16": list(quota), "reps": reps,
          "warmup": warmup, "B": L["B"], "Nb": L["Nb"], "Np": L["Np"], "N": w.N,
          "kept_pairs_per_head_16_8_4": [n16, n8, n4],
          "median_ms": {n: round(x, 4) for n, x in med.items()},
@@ -358,7 +363,9 @@ def sweep(args):
             sink.flush()
 
     for name in names:
-        w = synth.workload(name)
+        w = synth.workload(name).with_(fp4=args.fp4)
+        if args.fp4 == "nvfp4" and w.quota_bp[1] == 0:
+            continue  # no 4-bit pair in this workload: NVFP4 changes nothing
         reps = args.reps if args.reps else (5 if w.N > 200_000 else 20)
         print(f"# {name}: generating inputs", flush=True)
         Q, K, V = synth.make_inputs(w, threads=16)
@@ -369,16 +376,20 @@ def sweep(args):
         emit(base)
         kept = 10000 - w.quota_bp[0]
         if base["B"] == 128 and not args.own_only:
-            for lvl, quota in (("16", (w.quota_bp[0], 0, 0, kept)), ("8", (w.quota_bp[0], 0, kept, 0)),
-                               ("4", (w.quota_bp[0], kept, 0, 0))):
+            levels = (("16", (w.quota_bp[0], 0, 0, kept)), ("8", (w.quota_bp[0], 0, kept, 0)),
+                      ("4", (w.quota_bp[0], kept, 0, 0)))
+            if args.fp4 == "nvfp4":
+                levels = levels[2:]  # only the 4-bit level differs from the MXFP4 sweep
+            for lvl, quota in levels:
                 emit(measure_case(b, w, quota, q, k, v, dev, args.warmup, reps, stream,
                                   f"isolated_{lvl}bit"))
-            dense = measure_case(b, w, (0, 0, 0, 10000), q, k, v, dev, args.warmup, reps, stream,
-                                 "dense_16bit")
-            dense["speedup_attention"] = round(dense["median_ms"]["attention"] /
-                                               base["median_ms"]["attention"], 3)
-            dense["speedup_layer"] = round(dense["ms_per_layer"] / base["ms_per_layer"], 3)
-            emit(dense)
+            if args.fp4 != "nvfp4":
+                dense = measure_case(b, w, (0, 0, 0, 10000), q, k, v, dev, args.warmup, reps,
+                                     stream, "dense_16bit")
+                dense["speedup_attention"] = round(dense["median_ms"]["attention"] /
+                                                   base["median_ms"]["attention"], 3)
+                dense["speedup_layer"] = round(dense["ms_per_layer"] / base["ms_per_layer"], 3)
+                emit(dense)
         del q, k, v
         torch.cuda.empty_cache()
     if sink:
@@ -404,6 +415,8 @@ def main():
     ap.add_argument("--reps", type=int, default=0, help="timed layers per --sweep case")
     ap.add_argument("--own-only", action="store_true", help="--sweep: only each workload's quota")
     ap.add_argument("--out", default=None, help="--sweep: also write the JSON lines here")
+    ap.add_argument("--fp4", choices=["mxfp4", "nvfp4"], default="mxfp4",
+                    help="4-bit operand format (NVFP4: the pages' example format; MXFP4 default)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU (got --gpus {args.gpus}): the operator shards by heads "
@@ -418,7 +431,7 @@ def main():
     from video_dit_mixed_amd import binding as b
     from video_dit_mixed_amd import synth
 
-    w = synth.workload(args.workload)
+    w = synth.workload(args.workload).with_(fp4=args.fp4)
     if args.quota:
         w = w.with_(quota_bp=tuple(int(x) for x in args.quota.split(",")))
     # the CPU baseline's workers are forked now, before anything touches the GPU
@@ -470,12 +483,13 @@ def main():
     med = {n: statistics.median(v) for n, v in per.items()}
 
     heads_total = w.batch * w.heads
-    flops, t_roof, (n16, n8, n4) = roofline_terms(L, heads_total, w.head_dim)
+    flops, t_roof, (n16, n8, n4) = roofline_terms(L, heads_total, w.head_dim, w.fp4)
     t_attn = statistics.mean(per["attention"]) * 1e-3
     achieved = flops / t_attn
     peak = flops / t_roof
-    traffic = read_traffic(w.name) if not args.quota else None
-    dtype = "/".join(x for x, n in (("bf16", n16), ("i8+fp8", n8), ("mxfp4+fp8", n4)) if n > 0)
+    traffic = read_traffic(w.name) if not args.quota and args.fp4 == "mxfp4" else None
+    fp4_name = "nvfp4(bf16 mfma)+fp8" if w.fp4 == "nvfp4" else "mxfp4+fp8"
+    dtype = "/".join(x for x, n in (("bf16", n16), ("i8+fp8", n8), (fp4_name, n4)) if n > 0)
 
     res = {
         "metric": "ms/layer + % precision-weighted MFMA roofline, mixed-precision draft attn",
@@ -490,7 +504,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded blob+noise+outlier-channel Q/K, N(0,1) V)",
-        "config": {"workload": w.name, "batch": w.batch, "tokens": w.N, "latent": [w.T, w.H, w.W],
+        "config": {"workload": w.name, "fp4": w.fp4, "batch": w.batch, "tokens": w.N,
+                   "latent": [w.T, w.H, w.W],
                    "heads": w.heads, "head_dim": w.head_dim,
                    "region": [w.region_h, w.region_w], "lambda": w.lam,
                    "quota_bp_skip_4_8_16": list(w.quota_bp), "parallelism": "single GPU"},

@@ -33,8 +33,9 @@
  * Memory and ownership
  *   The caller owns every buffer: inputs, output and one workspace of dap_workspace_bytes() bytes.
  *   All pointers passed to the four calls are device pointers (map_out / scores_out too) and must
- *   be 256-byte aligned.  The library allocates nothing and keeps no global state; calls on
- *   different workspaces may run concurrently.  Work is enqueued on `stream` (0 = null stream)
+ *   be 256-byte aligned.  The library allocates nothing and, apart from the static scratch array
+ *   of dap_prepare_static_scratch, keeps no global state; calls on different workspaces may run
+ *   concurrently.  Work is enqueued on `stream` (0 = null stream)
  *   and the calls return without synchronising; buffers must stay alive until the enqueued work
  *   completes.  The four calls must be issued in the order prepare -> draft_rank -> attention ->
  *   restore on one workspace, in stream order.  The workspace carries a stage word (see

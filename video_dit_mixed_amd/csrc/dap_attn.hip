@@ -218,7 +218,7 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
                                           float& l_run, int np, int off, uint8_t* sK, uint8_t* sV,
                                           uint8_t* sKs, float* sBias) {
   using C = AttnCfg<B, D>;
-  const int n = c.n, gh = c.gh;
+  const int gh = c.gh;
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
   // Q operand for this phase, straight from the packed workspace
