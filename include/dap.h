@@ -173,11 +173,12 @@ dap_status dap_prepare(const dap_config* cfg, const void* q, const void* k, cons
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
- * loops, harnesses that forbid hipMalloc): dap_prepare with its scratch -- the per-channel V
- * maxima, batch*heads*head_dim 32-bit words -- held in a static device array of the library
- * (65536 words, 256 KiB, one copy per device, kept until the process ends) instead of the
- * workspace's v_amax section, which it leaves untouched.  Same arguments, results and errors as
- * dap_prepare, plus DAP_E_SCRATCH_LIMIT when batch*heads*head_dim exceeds 65536.  It allocates
+ * loops, harnesses that forbid hipMalloc): dap_prepare with its scratch -- the per-channel maxima
+ * of |V| and, when fp4_format is NVFP4, of |Q| and |K|, batch*heads*head_dim 32-bit words each --
+ * held in a static device array of the library (3 x 65536 words, 768 KiB, one copy per device,
+ * kept until the process ends) instead of the workspace's v_amax and qk_amax sections, which it
+ * leaves untouched.  Same arguments, results and errors as dap_prepare, plus DAP_E_SCRATCH_LIMIT
+ * when batch*heads*head_dim exceeds 65536.  It allocates
  * nothing: the array's device address is looked up once per device (hipGetSymbolAddress) on the
  * first call made with that device current; `stream` must belong to the current device.  All
  * calls on one device share the array and each clears it before use, so calls that can overlap

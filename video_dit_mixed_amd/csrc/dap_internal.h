@@ -121,8 +121,9 @@ hipError_t launch_attention(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_restore(const Geo& g, const Ws& w, uint16_t* out, hipStream_t s);
 hipError_t launch_stage(const Geo& g, const Ws& w, uint32_t accept, uint32_t next, hipStream_t s);
 
-// dap_prepare_static_scratch: the V channel maxima live in a static device array of this many
-// 32-bit words (256 KiB per device), so batch * heads * head_dim may not exceed it.
+// dap_prepare_static_scratch: the channel maxima of V (and of Q and K with NVFP4) live in a static
+// device array of three regions of this many 32-bit words (768 KiB per device), so
+// batch * heads * head_dim may not exceed it.
 constexpr size_t kStaticScratchWords = 65536;
 hipError_t launch_prepare_static_scratch(const Geo& g, const uint16_t* q, const uint16_t* k,
                                          const uint16_t* v, const Ws& w, hipStream_t s);

@@ -518,12 +518,14 @@ hipError_t launch_prepare(const Geo& g, const uint16_t* q, const uint16_t* k, co
 }
 
 // ------------------------------------------------------------------------------------ static scratch
-// The per-channel V maxima are the preparation's only scratch (written by v_amax_kernel, read by
-// v_pack_kernel in the same call).  dap_prepare_static_scratch keeps them in this array instead
-// of the caller's workspace.  Each device that loads the library holds its own copy until the
-// process ends; its address on the current device comes from hipGetSymbolAddress, taken once per
-// device.  In host code `scratch` names a host-side stand-in, never a device address.
-static __device__ __align__(256) uint32_t scratch[kStaticScratchWords];
+// The preparation's scratch is the per-channel maxima: of |V| (written by v_amax_kernel, read by
+// v_pack_kernel in the same call) and, with NVFP4, of |Q| and |K| (read by prep_qk_kernel for the
+// tensor scales).  dap_prepare_static_scratch keeps them in this array instead of the caller's
+// workspace: V's in words [0, bh*D), Q's and K's in [kStaticScratchWords, 3 kStaticScratchWords).
+// Each device that loads the library holds its own copy until the process ends; its address on
+// the current device comes from hipGetSymbolAddress, taken once per device.  In host code
+// `scratch` names a host-side stand-in, never a device address.
+static __device__ __align__(256) uint32_t scratch[3 * kStaticScratchWords];
 
 namespace {
 constexpr int kMaxDevices = 64;
@@ -554,7 +556,9 @@ hipError_t launch_prepare_static_scratch(const Geo& g, const uint16_t* q, const 
   const hipError_t e = static_scratch(&p);
   if (e != hipSuccess) return e;
   Ws ws = w;
-  ws.v_amax = p;  // cleared by prepare's own fill kernel before the maxima are taken
+  // each region is cleared by prepare's own fill kernels before its maxima are taken
+  ws.v_amax = p;
+  ws.qk_amax = p + kStaticScratchWords;  // used only when the 4-bit level is NVFP4
   return launch_prepare(g, q, k, v, ws, s);
 }
 
