@@ -507,6 +507,22 @@ def test_nvfp4_zero_tensor():
     _run_case(w, inputs=(Q, K, V))
 
 
+def test_nvfp4_vanishing_tensors():
+    # Tensors so small that NVFP4's fp32 steps leave the normal range (R30's zero rule): head 0's Q
+    # near 2^-116 (subnormal tensor scale, ordinary codes), head 1's K near 2^-128 (subnormal tensor
+    # scale, group steps whose reciprocal overflows: codes 0 under nonzero group scales), head 2's Q
+    # near 2^-132 (bf16 subnormals, mostly zeros), head 3's K near 2^-122 (subnormal steps with finite
+    # reciprocals).  Codes, group scales and tensor scales must match the oracle bit for bit.
+    w = synth.Workload("nvvanish", 4, 40, 64, 4, 128, 8, 16, 0.5, (4000, 3000, 1500, 1500), seed=4252,
+                       fp4="nvfp4")
+    Q, K, V = synth.make_inputs(w)
+    Q[0, 0] = _scaled_bits(Q[0, 0], 120)
+    K[0, 1] = _scaled_bits(K[0, 1], 132)
+    Q[0, 2] = _scaled_bits(Q[0, 2], 136)
+    K[0, 3] = _scaled_bits(K[0, 3], 126)
+    _run_case(w, inputs=(Q, K, V))
+
+
 @pytest.mark.parametrize("wi", [3, 4])
 def test_nvfp4_full_size(wi):
     w = synth.workload(wi).with_(fp4="nvfp4")
