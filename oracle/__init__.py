@@ -20,7 +20,7 @@ Modules, in pipeline order:
   dense      exact dense softmax attention (what the sparse operator approximates)
 
 Every function states the passage it follows.  Where the pages leave a step open, the reading used
-is stated in that function's module docstring as a numbered reading (R1..R29).
+is stated in that function's module docstring as a numbered reading (R1..R30).
 
 Parity status: every function is pinned by CPU tests (tests/test_oracle_*.py) against closed forms,
 library routines, exhaustive brute force or invariants.  The end-to-end numbers are "parity unpinned"

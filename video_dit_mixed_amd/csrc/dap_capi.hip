@@ -286,10 +286,7 @@ dap_status dap_draft_rank(const dap_config* cfg, void* ws, size_t ws_bytes, uint
   if (e == hipSuccess && map_out)
     e = hipMemcpyAsync(map_out, w.map, (size_t)g.bh * g.pairs, hipMemcpyDeviceToDevice, stream);
   if (e == hipSuccess)
-    e = dap::launch_stage(g, w,
-                          dap::stage_bit(DAP_STAGE_PREPARED) | dap::stage_bit(DAP_STAGE_RANKED) |
-                              dap::stage_bit(DAP_STAGE_ATTENDED),
-                          DAP_STAGE_RANKED, stream);
+    e = dap::launch_stage(g, w, dap::kAcceptDraftRank, DAP_STAGE_RANKED, stream);
   return hip_status(e);
 }
 
@@ -301,8 +298,7 @@ dap_status dap_attention(const dap_config* cfg, void* ws, size_t ws_bytes, hipSt
   const Ws w = make_ws(ws, L);
   hipError_t e = dap::launch_attention(g, w, stream);
   if (e == hipSuccess)
-    e = dap::launch_stage(g, w, dap::stage_bit(DAP_STAGE_RANKED) | dap::stage_bit(DAP_STAGE_ATTENDED),
-                          DAP_STAGE_ATTENDED, stream);
+    e = dap::launch_stage(g, w, dap::kAcceptAttention, DAP_STAGE_ATTENDED, stream);
   return hip_status(e);
 }
 

@@ -74,6 +74,16 @@ __host__ __device__ constexpr bool stage_ok(uint32_t cur, uint32_t t, uint32_t t
          (t == tag && (cur & kStageMagicMask) == kStageMagic && (cur & 0xffu) < 32u &&
           ((accept >> (cur & 0xffu)) & 1u) != 0u);
 }
+// The word a call leaves behind: its own stage when the words showed an accepted one, else BROKEN.
+__host__ __device__ constexpr uint32_t stage_after(uint32_t cur, uint32_t t, uint32_t tag,
+                                                   uint32_t accept, uint32_t next) {
+  return stage_ok(cur, t, tag, accept) ? next : (uint32_t)DAP_STAGE_BROKEN;
+}
+// What each call requires (dap_prepare accepts anything: kStageAny).
+constexpr uint32_t kAcceptDraftRank =
+    stage_bit(DAP_STAGE_PREPARED) | stage_bit(DAP_STAGE_RANKED) | stage_bit(DAP_STAGE_ATTENDED);
+constexpr uint32_t kAcceptAttention = stage_bit(DAP_STAGE_RANKED) | stage_bit(DAP_STAGE_ATTENDED);
+constexpr uint32_t kAcceptRestore = stage_bit(DAP_STAGE_ATTENDED);
 
 // Ranking: an 87-bit key per pair, ascending key = (score descending, pair index ascending):
 //   key = ((~bits(score) & 0x7fff'ffff'ffff'ffff) << 24) | pair_index, pair_index < 2^24.

@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void restore_kernel(Geo g, const uint16_t* __r
                                                       uint16_t* __restrict__ out) {
   // the packed output is only copied once attention has run on this workspace for this
   // configuration; otherwise the output is zeros
-  const bool ok = stage_ok(stage[0], stage[1], g.tag, stage_bit(DAP_STAGE_ATTENDED));
+  const bool ok = stage_ok(stage[0], stage[1], g.tag, kAcceptRestore);
   const int CH = g.D / 8;
   const size_t total = (size_t)g.bh * g.N * CH;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
