@@ -19,7 +19,11 @@ a 4-bit pair 1/10.1 + 1/5).
   --fp4 nvfp4 runs the 4-bit level in NVFP4 (the pages' example format) instead of MXFP4, on
            either leg (the GPU leg then takes only the allocations that have 4-bit pairs);
   --mx-rule ceil (cpu leg) takes MXFP4's alternative scale rule e = ceil(log2(amax/6)), which
-           never saturates, instead of the OCP rule floor(log2 amax) - 2 the path implements.
+           never saturates, instead of the OCP rule floor(log2 amax) - 2 the path implements;
+  --only A|B runs only the allocations whose name contains A or B.
+The last two allocations hold the attention time of 16-bit only (1125 bp) instead of its T_roof: their
+kept-pair counts come from the attention time per kept basis point measured on MI355X at the 720p layer
+(8-bit only 27.8 ms at 2250 bp; the 4/8 half/half mix 30.0 ms at 1505 + 1125 bp; 16-bit only 21.3 ms).
 
 rel-L2 = ||O - O_dense||_2 / ||O_dense||_2 over the rows taken; the bf16 rounding of the output
 alone gives about 1.1e-3.
@@ -78,6 +82,10 @@ def allocations():
         ("equal T_roof: 4/8 mix (half/half)", equal_budget(ref, (0.5, 0.5, 0)), 0.5),
         ("equal T_roof: 4/8/16 (1/3 each)", equal_budget(ref, (1 / 3, 1 / 3, 1 / 3)), 0.5),
         ("equal T_roof: 4/8 mix, avg-pool draft only", equal_budget(ref, (0.5, 0.5, 0)), 0.0),
+        # the pages compare at similar latency: kept-pair counts scaled so that the attention time
+        # on MI355X (measured per kept basis point on the 720p layer) matches 16-bit only at 1125 bp
+        ("equal measured time: 8-bit only", (8277, 0, 1723, 0), 0.5),
+        ("equal measured time: 4/8 half/half", (8132, 1069, 799, 0), 0.5),
     ]
     return rows
 
@@ -116,6 +124,8 @@ def gpu_leg(args):
     for name, quota, lam in allocations():
         if args.fp4 == "nvfp4" and quota[1] == 0:
             continue  # no 4-bit pair: the same result as with MXFP4
+        if args.only and not any(part in name for part in args.only.split("|")):
+            continue
         cfg = b.Config.from_workload(w, quota_bp=tuple(quota), lam=lam)
         ws = b.alloc_workspace(cfg, dev)
         b.forward(cfg, q, k, v, ws, out)
@@ -165,6 +175,8 @@ def cpu_leg(args):
     for name, quota, lam in allocations():
         if (args.fp4 == "nvfp4" or args.mx_rule != "ocp") and quota[1] == 0:
             continue  # no 4-bit pair: the same result as the default leg
+        if args.only and not any(part in name for part in args.only.split("|")):
+            continue
         t0 = time.perf_counter()
         got, exp = [], []
         for bh in range(w.batch * w.heads):
@@ -196,6 +208,8 @@ def main():
     ap.add_argument("--out", default=None)
     ap.add_argument("--fp4", choices=["mxfp4", "nvfp4"], default="mxfp4",
                     help="the 4-bit format of Q and K")
+    ap.add_argument("--only", default=None,
+                    help="only the allocations whose name contains one of these |-separated texts")
     ap.add_argument("--mx-rule", choices=["ocp", "ceil"], default="ocp",
                     help="cpu leg: MXFP4's scale rule (the path implements ocp)")
     args = ap.parse_args()
