@@ -23,7 +23,9 @@ dap_prepare -> dap_draft_rank -> dap_attention -> dap_restore.  Prints one JSON 
                 flops per launch (4*B^2*D per kept block pair) over its average duration from
                 HIP events on the launch stream; peak = flops / T_roof with T_roof the time every
                 kept pair would take at the dense peak of its own precisions (bf16 2.5 PF/s;
-                int8 and fp8 5.0 P/s; fp4 10.1 PF/s; NVFP4's Q.K^T, run as exact bf16, at 2.5)
+                int8 and fp8 5.0 P/s; fp4 10.1 PF/s; NVFP4's Q.K^T, run as exact bf16, at 2.5);
+                frac_at_sampled_sclk rescales the peaks (quoted at 2.4 GHz) to the median shader
+                clock sampled from sysfs during the timed steps (the "sclk" object)
   cpu_baseline  the CPU oracle on a bounded sample of the same workload (a process pool over heads,
                 one worker per core), extrapolated to a layer
 """
@@ -471,12 +473,15 @@ def main():
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    sampler = SclkSampler()
+    sampler.start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = sampler.stop()
     ms_per_step = wall * 1e3 / args.steps
     names = ["prepare", "draft_rank", "attention", "restore"]
     per = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
@@ -515,10 +520,14 @@ def main():
                      "traffic": traffic, "kernel": "attn_kernel",
                      "t_roof_ms": round(t_roof * 1e3, 4),
                      "kept_pairs_per_head_16_8_4": [n16, n8, n4]},
+        "sclk": sclk,
         "breakdown_ms_median": {n: round(v, 4) for n, v in med.items()},
         "t_roof_over_layer_ms": round(t_roof * 1e3 / ms_per_step, 4),
         "input_gen_s": round(t_gen, 1),
     }
+    if sclk and sclk.get("median_mhz"):
+        # the same fraction with the peaks scaled to the shader clock held during the timed steps
+        res["roofline"]["frac_at_sampled_sclk"] = round(achieved / peak * 2400.0 / sclk["median_mhz"], 4)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
