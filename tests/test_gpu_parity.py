@@ -275,9 +275,11 @@ def test_batch_two():
     _run_case(synth.workload(0).with_(batch=2))
 
 
-def test_ragged_odd_grid():
-    # regions that leave padding on both axes and an odd frame count
-    w = synth.Workload("ragged", 3, 13, 21, 2, 128, 8, 8, 0.5, (3000, 2500, 2500, 2000), seed=77)
+@pytest.mark.parametrize("fp4", ["mxfp4", "nvfp4"])
+def test_ragged_odd_grid(fp4):
+    # regions that leave padding on both axes and an odd frame count (64-token blocks, D = 128)
+    w = synth.Workload("ragged", 3, 13, 21, 2, 128, 8, 8, 0.5, (3000, 2500, 2500, 2000), seed=77,
+                       fp4=fp4)
     _run_case(w)
 
 
@@ -492,7 +494,7 @@ def test_nvfp4_block128_small(dims, quota):
     _run_case(w)
 
 
-@pytest.mark.parametrize("wi,D", [(0, 64), (0, 128), (1, 64)])
+@pytest.mark.parametrize("wi,D", [(0, 64), (0, 128), (1, 64), (1, 128)])
 def test_nvfp4_block16_and_64(wi, D):
     w = synth.workload(wi).with_(quota_bp=(2500, 5000, 1000, 1500), head_dim=D, heads=2, fp4="nvfp4")
     _run_case(w)
