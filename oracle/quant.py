@@ -198,7 +198,7 @@ def nvfp4(x: np.ndarray, amax=None):
       d    = f32(6 * t)
       s_g  = e4m3fn_rne_sat(f32(a_g / d))       group scale, a_g = max|x| over the group's 16
       step = f32(s_g * t);  inv = f32(1 / step) (0 when step is 0 or inv is not finite: the
-                                                 group's codes are then 0)
+                                                 group's magnitudes are then 0)
       code = E2M1_rne_sat(f32(|x| * inv)), bit 3 = the IEEE sign bit of x
     Returns (codes uint8 [..., D] 0..15, scale bytes uint8 [..., D/16] (e4m3fn), t float32)."""
     x = np.asarray(x, dtype=np.float64)

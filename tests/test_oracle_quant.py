@@ -278,10 +278,10 @@ def _nvfp4_reference(x):
             sg = Fraction(_e4m3_torch(float(_f32_rne(a_g / d))))
             sgs[idx + (g,)] = float(sg)
             step = _f32_rne(sg * t)
-            if step == 0:
-                continue
-            inv = _f32_rne(1 / step)
-            for i, v in enumerate(blk):
+            inv = _f32_rne(1 / step) if step > 0 else Fraction(0)
+            if inv >= Fraction(2) ** 128:   # the fp32 reciprocal rounds to infinity
+                inv = Fraction(0)
+            for i, v in enumerate(blk):     # magnitude 0 where inv is 0; the sign bit stays
                 y = _f32_rne(abs(v) * inv)
                 dist = [abs(y - gv) for gv in grid]
                 best = [k for k, dd in enumerate(dist) if dd == min(dist)]
@@ -357,6 +357,45 @@ def test_nvfp4_exact_on_representable_values_and_zero_tensor():
     codes, sg_code, tt = quant.nvfp4(y)
     i = np.unravel_index(np.argmax(np.abs(y)), y.shape)
     assert codes[i] & 7 == 7 and quant.e4m3fn_decode(sg_code[i[0], i[1] // 16]) == 448.0
+
+
+def test_nvfp4_vanishing_tensors_match_reference():
+    """Tensors small enough that the fp32 tensor scale and the group steps are subnormal, or that a
+    step's fp32 reciprocal overflows (the group's magnitudes are then 0, R30), against the exact
+    reference; bf16 subnormal inputs included."""
+    rng = np.random.default_rng(21)
+    base = rng.standard_normal((3, 32)) * np.array([[1.0], [0.05], [8.0]])
+    base[1, :16] = -np.abs(base[1, :16])     # an all-negative group: the sign bits must survive
+    for k in (116, 122, 126, 128, 132):
+        x = quant.bf16_rne(base * 2.0 ** -k)
+        codes, sg_code, t = quant.nvfp4(x)
+        rc, rsg, rt = _nvfp4_reference(x)
+        assert Fraction(float(t)) == rt, k
+        np.testing.assert_array_equal(quant.e4m3fn_decode(sg_code), rsg, err_msg=str(k))
+        np.testing.assert_array_equal(codes, rc, err_msg=str(k))
+    # the largest step is amax / 6; once that is below 1 / FLT_MAX (2^-132 here) every reciprocal
+    # overflows: all magnitudes 0, the signs kept
+    x = quant.bf16_rne(base * 2.0 ** -132)
+    codes, _, t = quant.nvfp4(x)
+    assert t > 0 and not (codes & 7).any()
+    assert ((codes >> 3) == np.signbit(x)).all()
+    # at 2^-128 the regimes mix: some groups keep finite reciprocals and nonzero codes
+    c128, _, _ = quant.nvfp4(quant.bf16_rne(base * 2.0 ** -128))
+    assert (c128 & 7).any() and not (c128[1] & 7).any()
+
+
+def test_nvfp4_scaled_value_rounds_in_fp32():
+    """R30 rounds |x| * inv to fp32 before the E2M1 rounding.  Found by search: with tensor maximum
+    1.5 and group maximum 0.65234375, inv = f32(1/step) = 9.33333302, and x = 0.1875 and 0.375 give
+    exact products just below the E2M1 ties 1.75 and 3.5 but fp32 products exactly on them, which
+    round to the even codes 4 (2.0) and 6 (4.0) instead of 3 and 5."""
+    row = np.zeros((1, 32))
+    row[0, :4] = [0.65234375, 0.1875, 0.375, -0.1875]
+    row[0, 16] = 1.5                         # the tensor maximum, in the second group
+    codes, sg_code, t = quant.nvfp4(row)
+    assert list(codes[0, 1:4]) == [4, 6, 8 | 4]
+    rc, rsg, rt = _nvfp4_reference(row)
+    np.testing.assert_array_equal(codes, rc)
 
 
 def test_mxfp4_ceil_rule_is_the_smallest_unsaturated_exponent():
