@@ -200,6 +200,30 @@ def test_prepared_operands_dequantise_to_their_own_tensor():
     assert np.all(np.abs(deq - r.vp)[big] <= np.abs(r.vp)[big] * 2.0 ** -4 * 1.0001)
 
 
+def test_nvfp4_operands_dequantise_to_their_own_tensor():
+    """With the 4-bit level in NVFP4 (R30) the 4-bit operands of a prepared head decode back to
+    their own packed Q and K within NVFP4's bound: half of the largest E2M1 spacing (two steps)
+    around the value, plus what saturation at 6 steps cuts off the group maximum, with a relative
+    slack of 2^-20 for the fp32 steps (they can move a value just past a tie onto it).  The MXFP4
+    operands of the same head break that bound (the outlier channels set coarse shared exponents),
+    so a pipeline that kept them would fail here."""
+    w = synth.workload(1)
+    q, k, v = synth.make_head(w, 3)
+    kw = dict(T=w.T, H=w.H, W=w.W, rh=w.region_h, rw=w.region_w, lam=w.lam, quota_bp=w.quota_bp)
+    r = pipeline.prepare_head(q, k, v, fp4_format="nvfp4", **kw)
+    rm = pipeline.prepare_head(q, k, v, fp4_format="mxfp4", **kw)
+    D = r.D
+    for x, val, mx_val, t in ((r.qp, r.q_fp4_val, rm.q_fp4_val, r.q_nv_t),
+                              (r.kp, r.k_fp4_val, rm.k_fp4_val, r.k_nv_t)):
+        assert float(t) == float(np.float32(np.float32(np.abs(x).max()) / np.float32(2688)))
+        amax_g = np.abs(x.reshape(-1, D // 16, 16)).max(axis=2)
+        sg = quant.e4m3fn_decode((r.q_nv_s if x is r.qp else r.k_nv_s)).astype(np.float64) * float(t)
+        bound = np.repeat(sg + np.maximum(amax_g - 6 * sg, 0.0), 16, axis=1).reshape(x.shape)
+        bound = bound * (1 + 2.0 ** -20) + 1e-300
+        assert np.all(np.abs(val - x) <= bound)
+        assert np.any(np.abs(mx_val - x) > bound)
+
+
 def test_dense_rows_match_torch_sdpa_and_softmax_identities():
     """The exact dense reference equals torch's fp64 scaled_dot_product_attention, and for V = I
     (D = N) its rows are the softmax probabilities: non-negative and summing to 1."""
