@@ -6,9 +6,10 @@
  * Figure 2 / Figure 3 captions).  One attention layer is four stream-ordered calls:
  *
  *   dap_prepare    reorder video tokens into compact spatial regions with padding, avg/max-pool
- *                  Q and K per region, quantise Q/K (per-block INT8, per-32-channel MXFP4) and
- *                  reorder + transpose + pack V (bf16 and per-channel FP8 e4m3)
- *                  -- blog section 方法概览 bullet 4, Figure 3 caption (a) and (b).
+ *                  Q and K per region, quantise Q/K (per-block INT8; the 4-bit level as
+ *                  per-32-channel MXFP4 or, per fp4_format, NVFP4) and reorder + transpose + pack
+ *                  V (bf16 and per-channel FP8 e4m3)
+ *                  -- blog section 方法概览 bullets 2 and 4, Figure 3 caption (a) and (b).
  *   dap_draft_rank build the lambda-mixed draft attention map from the pooled descriptors, rank all
  *                  region pairs of each head and assign 16-bit / 8-bit / 4-bit / skip by quota
  *                  -- blog section 方法概览 bullets 1 and 2; paper card AI Summary (shared sort).
@@ -52,7 +53,8 @@
  *
  * Errors
  *   Host-side validation runs before any HIP call and returns DAP_E_INVALID (null pointer, bad
- *   size, lambda outside [0, 1], negative quota or quota sum above 10000, misaligned pointer),
+ *   size, lambda outside [0, 1], negative quota or quota sum above 10000, misaligned pointer,
+ *   fp4_format neither DAP_FP4_MXFP4 nor DAP_FP4_NVFP4),
  *   DAP_E_UNSUPPORTED (head_dim not 64/128, region size not 16/64/128 tokens, more than 4096
  *   regions per head) or DAP_E_WORKSPACE (ws_bytes too small).  A failed kernel launch returns
  *   DAP_E_HIP.  Device faults surface at the caller's next synchronisation.  Non-finite inputs
@@ -195,7 +197,8 @@ dap_status dap_draft_rank(const dap_config* cfg, void* ws, size_t ws_bytes, uint
 
 /* Mixed-precision block-sparse attention over the block map; writes the packed output section
  * of the workspace.  16-bit blocks: bf16 Q K^T and bf16 P V; 8-bit: INT8 Q K^T and FP8 e4m3 P V;
- * 4-bit: MXFP4 Q K^T and FP8 e4m3 P V.  Phases run 16 -> 8 -> 4, key blocks ascending within a
+ * 4-bit: MXFP4 Q K^T (NVFP4: its exact values contracted in bf16, the tensor scales folded into
+ * the softmax scale) and FP8 e4m3 P V.  Phases run 16 -> 8 -> 4, key blocks ascending within a
  * phase, one running-max update per key block; a query block with no kept pair outputs 0. */
 dap_status dap_attention(const dap_config* cfg, void* ws, size_t ws_bytes, hipStream_t stream);
 
