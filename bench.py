@@ -72,22 +72,28 @@ def source_digest() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per attention launch from the committed counter summary, if it was taken on the
-    current kernel source for this workload; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
+def parse_traffic(text: str, workload: str, digest: str):
+    """HBM bytes per attention launch from the text of a counter summary, if it was taken on the
+    kernel source with this digest for this workload; else None."""
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in text.splitlines():
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("workload") != workload or kv.get("source_sha256_16") != source_digest():
+    if kv.get("workload") != workload or kv.get("source_sha256_16") != digest:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, if it was taken on the
+    current kernel source for this workload; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    return parse_traffic(open(TRAFFIC_FILE).read(), workload, source_digest())
 
 
 def _cpu_model() -> str:

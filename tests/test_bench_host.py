@@ -51,14 +51,10 @@ def test_pair_counts_follow_the_golden_quota_counts():
         assert got == (want["n16"], want["n8"], want["n4"]), name
 
 
-def test_traffic_is_reported_only_for_the_kernel_it_was_taken_on(tmp_path, monkeypatch):
-    f = tmp_path / "traffic.txt"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    body = "workload = hunyuan720p_33x45x80\nsource_sha256_16 = {}\nhbm_bytes_per_launch = 12345\n"
-    f.write_text(body.format(bench.source_digest()))
-    assert bench.read_traffic("hunyuan720p_33x45x80") == 12345.0
-    assert bench.read_traffic("fewstep_91x48x84") is None        # another workload
-    f.write_text(body.format("0" * 16))
-    assert bench.read_traffic("hunyuan720p_33x45x80") is None    # another kernel source
-    f.unlink()
-    assert bench.read_traffic("hunyuan720p_33x45x80") is None
+def test_traffic_is_reported_only_for_the_kernel_it_was_taken_on():
+    body = "# comment = ignored\nworkload = hunyuan720p_33x45x80\nsource_sha256_16 = {}\nhbm_bytes_per_launch = 12345\n"
+    d = bench.source_digest()
+    assert bench.parse_traffic(body.format(d), "hunyuan720p_33x45x80", d) == 12345.0
+    assert bench.parse_traffic(body.format(d), "fewstep_91x48x84", d) is None     # another workload
+    assert bench.parse_traffic(body.format("0" * 16), "hunyuan720p_33x45x80", d) is None  # another kernel
+    assert bench.parse_traffic("", "hunyuan720p_33x45x80", d) is None
