@@ -404,6 +404,17 @@ def sweep(args):
         sink.close()
 
 
+def lds_feed() -> int:
+    """Runs the stand-alone matrix-core / LDS timing program that build() compiles next to
+    libdap.so; it must have been built (no compilation happens here)."""
+    import subprocess
+    from video_dit_mixed_amd import build as bld
+    if not os.path.exists(bld.LDS_FEED_BENCH):
+        print(f"{bld.LDS_FEED_BENCH} is not built: run __graft_entry__.build() first", file=sys.stderr)
+        return 1
+    return subprocess.run([bld.LDS_FEED_BENCH]).returncode
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -425,7 +436,12 @@ def main():
     ap.add_argument("--out", default=None, help="--sweep: also write the JSON lines here")
     ap.add_argument("--fp4", choices=["mxfp4", "nvfp4"], default="mxfp4",
                     help="4-bit operand format (NVFP4: the pages' example format; MXFP4 default)")
+    ap.add_argument("--lds-feed", action="store_true",
+                    help="run the built lds_feed_bench program instead (matrix-core products fed "
+                         "from LDS, one workgroup per compute unit) and print its JSON lines")
     args = ap.parse_args()
+    if args.lds_feed:
+        sys.exit(lds_feed())
     if args.gpus != 1:
         print(f"bench.py measures one GPU (got --gpus {args.gpus}): the operator shards by heads "
               f"with no communication inside it, and the multi-GPU path is not implemented.",

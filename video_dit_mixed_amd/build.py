@@ -2,7 +2,9 @@
 
     python -m video_dit_mixed_amd.build            # compile every source, link the library
 
-Each .hip file is compiled for gfx950 only; the shared library lands next to this file.
+Each .hip file is compiled for gfx950 only; the shared library lands next to this file, and so
+does `lds_feed_bench`, a stand-alone timing program for matrix-core products fed from LDS
+(`python bench.py --lds-feed` runs it).
 Packed-fp32 instruction selection is disabled for all device code.
 """
 from __future__ import annotations
@@ -19,6 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdap.so")
+LDS_FEED_BENCH = os.path.join(HERE, "lds_feed_bench")
 
 SOURCES = ["dap_capi.hip", "dap_prep.hip", "dap_draft.hip", "dap_rank.hip", "dap_attn.hip",
            "dap_restore.hip", "dap_stage.hip"]
@@ -48,8 +51,14 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], os.path.join(CSRC, "lds_feed_bench.hip"),
+           "-o", LDS_FEED_BENCH + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for lds_feed_bench.hip:\n{r.stderr}")
+    os.replace(LDS_FEED_BENCH + ".tmp", LDS_FEED_BENCH)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {LDS_FEED_BENCH}")
     return LIB
 
 

@@ -1,0 +1,133 @@
+// How fast can gfx950's matrix cores run when their A operand comes from LDS?
+//
+// The attention kernel's products (S^T = K Q^T and O^T += V^T P^T) take the tile operand (K rows,
+// V^T rows) from LDS, one 16-byte read per lane -- 1 KB per wave -- per 32x32x16 bf16 product,
+// and the query-side operand from registers.  This program times that pattern in isolation: one
+// 512-thread workgroup per compute unit (two waves per SIMD, as in the attention kernel), each
+// wave looping over products and/or LDS reads, cycles taken with s_memtime (shader clock).
+//
+//   registers            products only, A from registers: the matrix-core peak (32 cycles each)
+//   lds_per_product      each product reads its A operand from LDS, scheduled by the compiler
+//   lds_per_two_products one read feeds two products (two B operands), half the LDS bytes
+//   lds_only             the reads alone, folded with XORs: the LDS read rate of a compute unit
+//
+// Prints one JSON line per pattern.  Reads are conflict-free (lane l reads 16 bytes at 16 l of a
+// 1 KB run), as are the attention kernel's swizzled operand reads.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kThreads = 512;
+constexpr int kSlots = 8192;  // 16-byte LDS slots: 128 KB, so one workgroup per compute unit
+constexpr int kUnroll = 8;
+
+enum Pattern { kRegisters, kLdsPerProduct, kLdsPerTwo, kLdsOnly, kPatterns };
+const char* const kNames[kPatterns] = {"registers", "lds_per_product", "lds_per_two_products", "lds_only"};
+
+__device__ __forceinline__ f32x16 mma(uint4 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void feed_kernel(unsigned long long* cycles, float* sink, int iters) {
+  __shared__ uint4 lds[kSlots];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kSlots; i += kThreads) lds[i] = make_uint4(3u * i, 5u * i + 1, 7u * i + 2, 0x3f803f80u);
+  __syncthreads();
+  const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(0x3f813f81u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  const uint4 areg = make_uint4(lane, lane + 1, lane + 2, 0x3f803f80u);
+  f32x16 acc[4] = {}, acc2[4] = {};
+  unsigned folded = 0;
+  int base = wave * 64 + lane;  // slot of this lane's first read; every index is taken mod kSlots
+  __syncthreads();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if constexpr (P == kRegisters) {
+        acc[u & 3] = mma(areg, b0, acc[u & 3]);
+      } else {
+        const uint4 v = lds[(base + 512 * u) & (kSlots - 1)];
+        if constexpr (P == kLdsPerProduct || P == kLdsPerTwo) acc[u & 3] = mma(v, b0, acc[u & 3]);
+        if constexpr (P == kLdsPerTwo) acc2[u & 3] = mma(v, b1, acc2[u & 3]);
+        if constexpr (P == kLdsOnly) folded ^= v.x ^ v.y ^ v.z ^ v.w;
+      }
+    }
+    base = (base + 4160) & (kSlots - 1);
+  }
+  __syncthreads();
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  if (tid == 0) cycles[blockIdx.x] = t1 - t0;
+  float s = (float)folded;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[k][r] + acc2[k][r];
+  sink[(size_t)blockIdx.x * kThreads + tid] = s;  // keeps every product and read live
+}
+
+template <int P>
+hipError_t launch(int grid, unsigned long long* cycles, float* sink, int iters) {
+  feed_kernel<P><<<grid, kThreads>>>(cycles, sink, iters);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    std::fprintf(stderr, "no HIP device\n");
+    return 1;
+  }
+  const int iters = argc > 1 ? std::min(std::max(std::atoi(argv[1]), 1), 1000000) : 4000;
+  const int grid = cus;  // one workgroup per compute unit
+  unsigned long long* d_cycles = nullptr;
+  float* d_sink = nullptr;
+  if (hipMalloc(&d_cycles, sizeof(unsigned long long) * grid) != hipSuccess ||
+      hipMalloc(&d_sink, sizeof(float) * (size_t)grid * kThreads) != hipSuccess) {
+    std::fprintf(stderr, "hipMalloc failed\n");
+    return 1;
+  }
+  unsigned long long* h = new unsigned long long[grid];
+  for (int p = 0; p < kPatterns; ++p) {
+    for (int rep = 0; rep < 2; ++rep) {  // the first run warms the clocks up
+      hipError_t e = p == kRegisters       ? launch<kRegisters>(grid, d_cycles, d_sink, iters)
+                     : p == kLdsPerProduct ? launch<kLdsPerProduct>(grid, d_cycles, d_sink, iters)
+                     : p == kLdsPerTwo     ? launch<kLdsPerTwo>(grid, d_cycles, d_sink, iters)
+                                           : launch<kLdsOnly>(grid, d_cycles, d_sink, iters);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      if (e != hipSuccess) {
+        std::fprintf(stderr, "%s: %s\n", kNames[p], hipGetErrorString(e));
+        return 1;
+      }
+    }
+    if (hipMemcpy(h, d_cycles, sizeof(unsigned long long) * grid, hipMemcpyDeviceToHost) != hipSuccess) return 1;
+    double avg = 0;
+    for (int i = 0; i < grid; ++i) avg += (double)h[i];
+    avg /= grid;
+    // per SIMD: two waves, kUnroll reads or products per wave and iteration (two products per
+    // read in lds_per_two_products); per compute unit: eight waves of 1 KB reads
+    const double units = 2.0 * iters * kUnroll * (p == kLdsPerTwo ? 2 : 1);
+    const double lds_bytes = p == kRegisters ? 0.0 : 8.0 * iters * kUnroll * 1024;
+    const double per = avg / units;
+    char frac[32] = "null";  // a 32x32x16 bf16 product takes 32 cycles at the peak
+    if (p != kLdsOnly) std::snprintf(frac, sizeof(frac), "%.3f", 32.0 / per);
+    std::printf("{\"pattern\": \"%s\", \"cycles\": %.0f, \"cycles_per_%s_per_simd\": %.2f, "
+                "\"matrix_core_fraction\": %s, \"lds_bytes_per_clk_per_cu\": %.1f, \"cus\": %d}\n",
+                kNames[p], avg, p == kLdsOnly ? "read" : "product", per, frac, lds_bytes / avg, cus);
+  }
+  delete[] h;
+  hipFree(d_cycles);
+  hipFree(d_sink);
+  return 0;
+}
