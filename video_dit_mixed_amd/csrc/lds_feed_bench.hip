@@ -9,6 +9,9 @@
 //   registers            products only, A from registers: the matrix-core peak (32 cycles each)
 //   lds_per_product      each product reads its A operand from LDS, scheduled by the compiler
 //   lds_per_two_products one read feeds two products (two B operands), half the LDS bytes
+//   lds_softmax_valu     lds_per_product plus, per product, the vector work of the attention kernel's
+//                        16-bit phase per product: one exponential (two issue slots) and four other
+//                        instructions, about 25 VALU cycles, in independent chains
 //   lds_only             the reads alone, folded with XORs: the LDS read rate of a compute unit
 //
 // Prints one JSON line per pattern.  Reads are conflict-free (lane l reads 16 bytes at 16 l of a
@@ -29,8 +32,9 @@ constexpr int kThreads = 512;
 constexpr int kSlots = 8192;  // 16-byte LDS slots: 128 KB, so one workgroup per compute unit
 constexpr int kUnroll = 8;
 
-enum Pattern { kRegisters, kLdsPerProduct, kLdsPerTwo, kLdsOnly, kPatterns };
-const char* const kNames[kPatterns] = {"registers", "lds_per_product", "lds_per_two_products", "lds_only"};
+enum Pattern { kRegisters, kLdsPerProduct, kLdsPerTwo, kLdsSoftmaxValu, kLdsOnly, kPatterns };
+const char* const kNames[kPatterns] = {"registers", "lds_per_product", "lds_per_two_products",
+                                       "lds_softmax_valu", "lds_only"};
 
 __device__ __forceinline__ f32x16 mma(uint4 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
@@ -47,27 +51,37 @@ __global__ __launch_bounds__(kThreads) void feed_kernel(unsigned long long* cycl
   const uint4 areg = make_uint4(lane, lane + 1, lane + 2, 0x3f803f80u);
   f32x16 acc[4] = {}, acc2[4] = {};
   unsigned folded = 0;
-  int base = wave * 64 + lane;  // slot of this lane's first read; every index is taken mod kSlots
+  float ch[4] = {0.25f * lane, 0.5f, -0.75f, 1.0f};  // independent vector chains (lds_softmax_valu)
+  const float cs = 0.0625f, nb = -0.5f;
+  const int lane_slot = wave * 64 + lane;  // < 512
   __syncthreads();
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   for (int it = 0; it < iters; ++it) {
+    // reads at base + 512 u, u < 8: base <= 7 * 512 + 511, so every slot is at most 7679 < kSlots,
+    // and each read is the base register plus a constant offset
+    const int base = (it & 7) * 512 + lane_slot;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if constexpr (P == kRegisters) {
         acc[u & 3] = mma(areg, b0, acc[u & 3]);
       } else {
-        const uint4 v = lds[(base + 512 * u) & (kSlots - 1)];
-        if constexpr (P == kLdsPerProduct || P == kLdsPerTwo) acc[u & 3] = mma(v, b0, acc[u & 3]);
+        const uint4 v = lds[base + 512 * u];
+        if constexpr (P == kLdsPerProduct || P == kLdsPerTwo || P == kLdsSoftmaxValu) acc[u & 3] = mma(v, b0, acc[u & 3]);
+        if constexpr (P == kLdsSoftmaxValu) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(ch[u & 3], cs, nb));
+          ch[(u + 1) & 3] = fmaf(ch[(u + 1) & 3], 0.99f, e);
+          ch[(u + 2) & 3] = fmaxf(ch[(u + 2) & 3], e);
+          ch[(u + 3) & 3] = ch[(u + 3) & 3] + e;
+        }
         if constexpr (P == kLdsPerTwo) acc2[u & 3] = mma(v, b1, acc2[u & 3]);
         if constexpr (P == kLdsOnly) folded ^= v.x ^ v.y ^ v.z ^ v.w;
       }
     }
-    base = (base + 4160) & (kSlots - 1);
   }
   __syncthreads();
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
   if (tid == 0) cycles[blockIdx.x] = t1 - t0;
-  float s = (float)folded;
+  float s = (float)folded + ch[0] + ch[1] + ch[2] + ch[3];
 #pragma unroll
   for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -104,6 +118,7 @@ int main(int argc, char** argv) {
       hipError_t e = p == kRegisters       ? launch<kRegisters>(grid, d_cycles, d_sink, iters)
                      : p == kLdsPerProduct ? launch<kLdsPerProduct>(grid, d_cycles, d_sink, iters)
                      : p == kLdsPerTwo     ? launch<kLdsPerTwo>(grid, d_cycles, d_sink, iters)
+                     : p == kLdsSoftmaxValu ? launch<kLdsSoftmaxValu>(grid, d_cycles, d_sink, iters)
                                            : launch<kLdsOnly>(grid, d_cycles, d_sink, iters);
       if (e == hipSuccess) e = hipDeviceSynchronize();
       if (e != hipSuccess) {
