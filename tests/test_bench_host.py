@@ -58,3 +58,11 @@ def test_traffic_is_reported_only_for_the_kernel_it_was_taken_on():
     assert bench.parse_traffic(body.format(d), "fewstep_91x48x84", d) is None     # another workload
     assert bench.parse_traffic(body.format("0" * 16), "hunyuan720p_33x45x80", d) is None  # another kernel
     assert bench.parse_traffic("", "hunyuan720p_33x45x80", d) is None
+
+
+def test_lds_feed_needs_the_built_program(monkeypatch, capsys):
+    """`bench.py --lds-feed` runs only what build() compiled; a missing program is an error, not a build."""
+    from video_dit_mixed_amd import build as bld
+    monkeypatch.setattr(bld, "LDS_FEED_BENCH", os.path.join(os.path.dirname(__file__), "no_such_program"))
+    assert bench.lds_feed() == 1
+    assert "not built" in capsys.readouterr().err

@@ -8,6 +8,7 @@
 //
 //   registers            products only, A from registers: the matrix-core peak (32 cycles each)
 //   lds_per_product      each product reads its A operand from LDS, scheduled by the compiler
+//   lds_b_operand        the same with the LDS operand in the B position (A from registers)
 //   lds_per_two_products one read feeds two products (two B operands), half the LDS bytes
 //   lds_softmax_valu     lds_per_product plus, per product, the vector work of the attention kernel's
 //                        16-bit phase per product: one exponential (two issue slots) and four other
@@ -32,12 +33,15 @@ constexpr int kThreads = 512;
 constexpr int kSlots = 8192;  // 16-byte LDS slots: 128 KB, so one workgroup per compute unit
 constexpr int kUnroll = 8;
 
-enum Pattern { kRegisters, kLdsPerProduct, kLdsPerTwo, kLdsSoftmaxValu, kLdsOnly, kPatterns };
-const char* const kNames[kPatterns] = {"registers", "lds_per_product", "lds_per_two_products",
+enum Pattern { kRegisters, kLdsPerProduct, kLdsB, kLdsPerTwo, kLdsSoftmaxValu, kLdsOnly, kPatterns };
+const char* const kNames[kPatterns] = {"registers", "lds_per_product", "lds_b_operand", "lds_per_two_products",
                                        "lds_softmax_valu", "lds_only"};
 
 __device__ __forceinline__ f32x16 mma(uint4 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_b(uint4 a, uint4 b, f32x16 c) {  // b in the B position
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 template <int P>
@@ -67,6 +71,7 @@ __global__ __launch_bounds__(kThreads) void feed_kernel(unsigned long long* cycl
       } else {
         const uint4 v = lds[base + 512 * u];
         if constexpr (P == kLdsPerProduct || P == kLdsPerTwo || P == kLdsSoftmaxValu) acc[u & 3] = mma(v, b0, acc[u & 3]);
+        if constexpr (P == kLdsB) acc[u & 3] = mma_b(areg, v, acc[u & 3]);
         if constexpr (P == kLdsSoftmaxValu) {
           const float e = __builtin_amdgcn_exp2f(fmaf(ch[u & 3], cs, nb));
           ch[(u + 1) & 3] = fmaf(ch[(u + 1) & 3], 0.99f, e);
@@ -117,6 +122,7 @@ int main(int argc, char** argv) {
     for (int rep = 0; rep < 2; ++rep) {  // the first run warms the clocks up
       hipError_t e = p == kRegisters       ? launch<kRegisters>(grid, d_cycles, d_sink, iters)
                      : p == kLdsPerProduct ? launch<kLdsPerProduct>(grid, d_cycles, d_sink, iters)
+                     : p == kLdsB          ? launch<kLdsB>(grid, d_cycles, d_sink, iters)
                      : p == kLdsPerTwo     ? launch<kLdsPerTwo>(grid, d_cycles, d_sink, iters)
                      : p == kLdsSoftmaxValu ? launch<kLdsSoftmaxValu>(grid, d_cycles, d_sink, iters)
                                            : launch<kLdsOnly>(grid, d_cycles, d_sink, iters);
