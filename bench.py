@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --sweep [--workloads A,B,...] [--out FILE]
+    python bench.py --section-clocks [--workload NAME] [--quota Q] [--fp4 F]   # where the waves' cycles go
+    python bench.py --lds-feed                                                 # matrix-core / LDS program
 
 The --sweep mode measures every workload (all five by default), one JSON line per case:
   * the workload's own quota: per-call median and minimum over R timed layers (R = 20, 5 for the
@@ -415,6 +417,46 @@ def lds_feed() -> int:
     return subprocess.run([bld.LDS_FEED_BENCH]).returncode
 
 
+def section_clocks(w) -> dict:
+    """One attention launch of the section-clock diagnostic after two plain ones: per precision
+    phase, the cycles per wave-block and the share of each part of the key-block loop (the
+    clocked instance reads the shader clock, so its launch is a few per cent slower)."""
+    import torch
+    from video_dit_mixed_amd import binding as b
+    from video_dit_mixed_amd import synth
+    cfg = b.Config.from_workload(w)
+    dev = torch.device("cuda:0")
+    Q, K, V = synth.make_inputs(w, threads=16)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(Q), to(K), to(V)
+    del Q, K, V
+    ws = b.alloc_workspace(cfg, dev)
+    b.prepare(cfg, q, k, v, ws)
+    b.draft_rank(cfg, ws)
+    for _ in range(2):
+        b.attention(cfg, ws)
+    clk = torch.zeros(b.SECTION_CLOCK_WORDS, dtype=torch.int64, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    b.attention_section_clocks(cfg, ws, clk, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    c = clk.cpu().numpy().astype(np.uint64).astype(np.float64).reshape(4, 8)
+    names = ("16-bit", "8-bit", "4-bit MXFP4", "4-bit NVFP4")
+    phases = {}
+    for p in range(4):
+        if c[p, 6] == 0:
+            continue
+        tot = c[p, :6].sum()
+        phases[names[p]] = {"wave_blocks": int(c[p, 6]),
+                            "cycles_per_wave_block": round(tot / c[p, 6], 1),
+                            "share_of_wave_cycles": round(tot / c[0, 7], 4),
+                            **{n: round(c[p, i] / tot, 4) for i, n in enumerate(b.SECTION_CLOCK_PARTS)}}
+    return {"section_clocks": {"workload": w.name, "quota_bp": list(w.quota_bp), "fp4": w.fp4,
+                               "clocked_launch_ms": round(e0.elapsed_time(e1), 3), "phases": phases}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,6 +481,9 @@ def main():
     ap.add_argument("--lds-feed", action="store_true",
                     help="run the built lds_feed_bench program instead (matrix-core products fed "
                          "from LDS, one workgroup per compute unit) and print its JSON lines")
+    ap.add_argument("--section-clocks", action="store_true",
+                    help="instead of timing, run dap_attention_section_clocks once on the workload "
+                         "(and --quota / --fp4) and print where the attention waves spend their cycles")
     args = ap.parse_args()
     if args.lds_feed:
         sys.exit(lds_feed())
@@ -458,6 +503,9 @@ def main():
     w = synth.workload(args.workload).with_(fp4=args.fp4)
     if args.quota:
         w = w.with_(quota_bp=tuple(int(x) for x in args.quota.split(",")))
+    if args.section_clocks:
+        print(json.dumps(section_clocks(w)), flush=True)
+        return
     # the CPU baseline's workers are forked now, before anything touches the GPU
     cpu = None if args.no_cpu_baseline else CpuBaseline(w)
     if not torch.cuda.is_available():

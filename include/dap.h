@@ -202,6 +202,24 @@ dap_status dap_draft_rank(const dap_config* cfg, void* ws, size_t ws_bytes, uint
  * phase, one running-max update per key block; a query block with no kept pair outputs 0. */
 dap_status dap_attention(const dap_config* cfg, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Diagnostic for profiling the attention kernel: dap_attention (same output, same stage
+ * transition, same errors) run by a second instance of its kernel that reads the shader clock
+ * (s_memtime) around each part of the key-block loop.  Per precision phase p (0: 16-bit, 1: 8-bit,
+ * 2: MXFP4 4-bit, 3: NVFP4 4-bit) it adds, summed over waves, into clocks[8 p + i]:
+ *   i = 0  cycles from the start of a key block until its K tile has landed (the wait, and the
+ *          bias / scale stores and, for blocks below 128 tokens, the K stores into LDS)
+ *       1  in the first barrier
+ *       2  in Q K^T, the softmax statistics and the rescale of the output accumulator
+ *       3  waiting for the V tile (for blocks below 128 tokens, also storing it into LDS)
+ *       4  in the second barrier
+ *       5  in P V and the next K tile's load issue
+ *       6  wave-blocks counted (one wave of 32 queries against one key block)
+ * and clocks[7] the summed lifetimes of the waves, in the same cycles.  clocks: device uint64_t[32],
+ * 8-byte aligned, added to (zero it first); DAP_E_INVALID if null or misaligned.  Reading the clock
+ * makes this run a few per cent slower than dap_attention. */
+dap_status dap_attention_section_clocks(const dap_config* cfg, void* ws, size_t ws_bytes,
+                                        uint64_t* clocks, hipStream_t stream);
+
 /* Packed output -> out (device bf16 [batch, heads, N, D]) in the original token order. */
 dap_status dap_restore(const dap_config* cfg, const void* ws, size_t ws_bytes, void* out,
                        hipStream_t stream);

@@ -85,6 +85,11 @@ def test_calls_validate_before_touching_the_device():
     assert lib.dap_attention(P(bad), 256, need, None) == b.DAP_E_UNSUPPORTED
     assert lib.dap_prepare_static_scratch(P(c), None, 256, 256, 256, need, None) == b.DAP_E_INVALID
     assert lib.dap_prepare_static_scratch(P(c), 256, 256, 256, 256, need - 1, None) == b.DAP_E_WORKSPACE
+    # the section-clock diagnostic: the workspace checks of dap_attention, then its counter buffer
+    assert lib.dap_attention_section_clocks(P(c), 256, need - 1, 256, None) == b.DAP_E_WORKSPACE
+    assert lib.dap_attention_section_clocks(P(c), 256, need, None, None) == b.DAP_E_INVALID
+    assert lib.dap_attention_section_clocks(P(c), 256, need, 260, None) == b.DAP_E_INVALID
+    assert lib.dap_attention_section_clocks(P(bad), 256, need, 256, None) == b.DAP_E_UNSUPPORTED
 
 
 def test_static_scratch_limit_is_checked_on_the_host():
@@ -175,6 +180,10 @@ def test_binding_checks_tensors_before_the_library_call():
         b.restore(cfg, ws, torch.zeros((1, 1), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="bytes"):
         b.draft_rank(cfg, ws, map_out=torch.zeros(3, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="shape"):
+        b.attention_section_clocks(cfg, 256, torch.zeros(31, dtype=torch.int64))
+    with pytest.raises(ValueError, match="dtype"):
+        b.attention_section_clocks(cfg, 256, torch.zeros(b.SECTION_CLOCK_WORDS, dtype=torch.int32))
 
 
 def _oracle_imports(path):

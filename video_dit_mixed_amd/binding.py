@@ -24,8 +24,11 @@ STAGE_PREPARED, STAGE_RANKED, STAGE_ATTENDED, STAGE_BROKEN = (0xDA900001, 0xDA90
 FP4_MXFP4, FP4_NVFP4 = 0, 1
 LEVEL_SKIP, LEVEL_4, LEVEL_8, LEVEL_16 = 0, 1, 2, 3
 EXPORTED = ("dap_abi_version", "dap_workspace_bytes", "dap_workspace_layout", "dap_prepare",
-            "dap_prepare_static_scratch", "dap_draft_rank", "dap_attention", "dap_restore",
-            "dap_status_string")
+            "dap_prepare_static_scratch", "dap_draft_rank", "dap_attention",
+            "dap_attention_section_clocks", "dap_restore", "dap_status_string")
+# dap_attention_section_clocks: counters per phase (16-bit, 8-bit, MXFP4, NVFP4), in this order
+SECTION_CLOCK_PARTS = ("wait_k", "barrier_1", "qk_and_statistics", "wait_v", "barrier_2", "pv")
+SECTION_CLOCK_WORDS = 32
 
 
 class DapError(RuntimeError):
@@ -123,6 +126,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dap_draft_rank.argtypes = [P(_Config), vp, ctypes.c_size_t, vp, vp, vp]
     lib.dap_attention.restype = ctypes.c_int
     lib.dap_attention.argtypes = [P(_Config), vp, ctypes.c_size_t, vp]
+    lib.dap_attention_section_clocks.restype = ctypes.c_int
+    lib.dap_attention_section_clocks.argtypes = [P(_Config), vp, ctypes.c_size_t, vp, vp]
     lib.dap_restore.restype = ctypes.c_int
     lib.dap_restore.argtypes = [P(_Config), vp, ctypes.c_size_t, vp, vp]
     lib.dap_status_string.restype = ctypes.c_char_p
@@ -248,6 +253,17 @@ def attention(cfg: Config, ws, stream=None):
     c = cfg.c_struct()
     _check(load().dap_attention(ctypes.byref(c), _ptr(ws), _nbytes(ws), _stream(stream)),
            "dap_attention")
+
+
+def attention_section_clocks(cfg: Config, ws, clocks, stream=None):
+    """dap_attention with the kernel's shader-clock counters added into `clocks` (a zeroed int64
+    device tensor of SECTION_CLOCK_WORDS; word 8 p + i is part i of phase p, word 8 p + 6 the
+    wave-blocks of phase p, word 7 the summed wave lifetimes)."""
+    _expect(ws, "ws", "uint8")
+    _expect(clocks, "clocks", "int64", (SECTION_CLOCK_WORDS,))
+    c = cfg.c_struct()
+    _check(load().dap_attention_section_clocks(ctypes.byref(c), _ptr(ws), _nbytes(ws), _ptr(clocks),
+                                               _stream(stream)), "dap_attention_section_clocks")
 
 
 def restore(cfg: Config, ws, out, stream=None):

@@ -210,13 +210,20 @@ __device__ __forceinline__ const uint8_t* v_tile_src(const Geo& g, const Ws& w, 
              : w.vt_fp8 + ((size_t)bh * g.Nb + kb) * (size_t)D * C::KP8;
 }
 
+// Section clocks (the diagnostic instantiation only): per phase, the shader-clock cycles of the
+// key-block loop's parts summed over waves -- 0 wait for K, 1 first barrier, 2 Q K^T and the
+// statistics, 3 wait for V, 4 second barrier, 5 P V -- then 6 the wave-blocks counted and, in phase
+// 0's row, 7 the summed lifetimes of the waves.
+constexpr int kClkPerPhase = 8;
+__device__ __forceinline__ unsigned long long clk_now() { return __builtin_amdgcn_s_memtime(); }
+
 // All key blocks of one precision phase (PH = 0: 16-bit, 1: 8-bit, 2: 4-bit) for this row.
 // Only this phase's Q operand is live, so the three phases do not compete for registers.
-template <int B, int D, int PH>
+template <int B, int D, int PH, bool kClk>
 __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCtx& c,
                                           f32x16 (&O)[AttnCfg<B, D>::DT], float& m_run,
                                           float& l_run, int np, int off, uint8_t* sK, uint8_t* sV,
-                                          uint8_t* sKs, float* sBias) {
+                                          uint8_t* sKs, float* sBias, unsigned long long* clk) {
   using C = AttnCfg<B, D>;
   const int gh = c.gh;
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
@@ -262,7 +269,16 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
                  ? *reinterpret_cast<const uint32_t*>(w.k_e8m0 + ((size_t)c.bh * g.Np + (size_t)kb * B) * (D / 32) + 4 * c.tid)
                  : 0x7f7f7f7fu;
 
+  unsigned long long ck[6] = {0, 0, 0, 0, 0, 0}, t_prev = 0;
+  auto tick = [&](int part) {  // adds the cycles since the previous tick to part
+    if constexpr (kClk) {
+      const unsigned long long t = clk_now();
+      if (part >= 0) ck[part] += t - t_prev;
+      t_prev = t;
+    }
+  };
   for (int it = 0; it < np; ++it) {
+    tick(-1);
     // consumed at the end of this iteration (its latency hides behind the barrier and Q K^T)
     const int kb_next = list_at(c, off + min(it + 1, np - 1));  // the last block re-reads its own entry
     const float sk_next = PH == 1 ? __uint_as_float(uniform_load(reinterpret_cast<const uint32_t*>(ks8) + kb_next)) : 0.0f;
@@ -283,7 +299,9 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
       sBias[m] = (m < B && iy < vh && ix < vw) ? 0.0f : -INFINITY;
     }
     if constexpr (C::DIRECT) wait_vm<0>();  // K (issued one key block earlier) has landed
+    tick(0);
     bar();  // K, scales and bias visible; every wave is done with the previous P V
+    tick(1);
     // This tile's V streams in while Q K^T and the softmax run; its loads are issued a quarter after
     // each m-tile's products, so the first products do not wait behind the whole tile's issue.
     constexpr int NVL = TileMover<D, P::VRC, C::NT, C::DIRECT>::N;
@@ -415,9 +433,12 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     // block's K streams in during the products.  P is produced chunk by chunk right before the
     // products that consume it, so its exponentials can run under the previous chunk's
     // matrix-core work.
+    tick(2);
     if constexpr (C::DIRECT) wait_vm<0>();
     vt.commit(sV, c.tid);
+    tick(3);
     bar();  // V visible; every wave is done with sK
+    tick(4);
     // The P V section carries most of the VALU work; the other wave on the SIMD is then usually in
     // its Q K^T, which needs the matrix core far more than the VALU.  Raising this wave's issue
     // priority while its exponentials run lets both proceed (16- and 8-bit phases: -0.5 to -1.5 %
@@ -495,14 +516,24 @@ __device__ __forceinline__ void run_phase(const Geo& g, const Ws& w, const RowCt
     l_run = alpha * l_run + psum;
     kb = kb_next;
     sk = sk_next;
+    tick(5);
+  }
+  if constexpr (kClk) {
+    if ((c.tid & 63) == 0) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) atomicAdd(clk + PH * kClkPerPhase + i, ck[i]);
+      atomicAdd(clk + PH * kClkPerPhase + 6, (unsigned long long)np);
+    }
   }
 }
 
 // kNv: the 4-bit level runs in NVFP4 (phase 3) instead of MXFP4 (phase 2); a separate
 // instantiation, so that each kernel holds the registers of its own phases only
-template <int B, int D, bool kNv>
+// kClk: the section-clock diagnostic (clk holds 4 x kClkPerPhase counters); off, the kernel
+// reads no clock and clk is unused
+template <int B, int D, bool kNv, bool kClk>
 __global__ __launch_bounds__(64 * (B >= 32 ? B / 32 : 1)) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_kernel(Geo g, Ws w) {
+void attn_kernel(Geo g, Ws w, unsigned long long* clk) {
   using C = AttnCfg<B, D>;
   __shared__ __attribute__((aligned(16))) uint8_t sK[C::KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sV[C::VBYTES];
@@ -511,6 +542,8 @@ void attn_kernel(Geo g, Ws w) {
 
   // Workgroups are dispatched round-robin over the 8 dies: workgroup id x + 8j runs on die x and
   // takes entry j of that die's slice of the work order.
+  unsigned long long t_start = 0;
+  if constexpr (kClk) t_start = clk_now();
   RowCtx c;
   const int Nb = g.Nb;
   if (!stage_ok(uniform_load(w.stage), uniform_load(w.stage + 1), g.tag,
@@ -555,7 +588,7 @@ void attn_kernel(Geo g, Ws w) {
     for (int r = 0; r < 16; ++r) O[i][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  if (n16 > 0) run_phase<B, D, 0>(g, w, c, O, m_run, l_run, n16, 0, sK, sV, sKs, sBias);
+  if (n16 > 0) run_phase<B, D, 0, kClk>(g, w, c, O, m_run, l_run, n16, 0, sK, sV, sKs, sBias, clk);
   const bool lowbit = n8 + n4 > 0;
   // The FP8 V scales of this lane's accumulator channels 32 dt + 8 r4 + 4 gh + e: four
   // consecutive channels per (dt, r4), fetched together as 16-byte loads.
@@ -581,8 +614,8 @@ void attn_kernel(Geo g, Ws w) {
         for (int e = 0; e < 4; ++e) O[dt][4 * r4 + e] = s4[e] > 0.0f ? (O[dt][4 * r4 + e] * 256.0f) / s4[e] : 0.0f;
       }
   }
-  if (n8 > 0) run_phase<B, D, 1>(g, w, c, O, m_run, l_run, n8, n16, sK, sV, sKs, sBias);
-  if (n4 > 0) run_phase<B, D, kNv ? 3 : 2>(g, w, c, O, m_run, l_run, n4, n16 + n8, sK, sV, sKs, sBias);
+  if (n8 > 0) run_phase<B, D, 1, kClk>(g, w, c, O, m_run, l_run, n8, n16, sK, sV, sKs, sBias, clk);
+  if (n4 > 0) run_phase<B, D, kNv ? 3 : 2, kClk>(g, w, c, O, m_run, l_run, n4, n16 + n8, sK, sV, sKs, sBias, clk);
 
   // ---- finalise: O / l (0 when no pair was kept), undo the low-bit units, bf16 out
   const float l = halves_sum(l_run);
@@ -612,30 +645,42 @@ void attn_kernel(Geo g, Ws w) {
         *reinterpret_cast<uint2*>(dst + d0) = make_uint2(lo, hi);
       }
   }
+  if constexpr (kClk) {
+    if ((c.tid & 63) == 0) atomicAdd(clk + 7, clk_now() - t_start);
+  }
 }
 
-template <int B, int D>
-hipError_t attn_bd(const Geo& g, const Ws& w, hipStream_t s) {
+template <int B, int D, bool kClk>
+hipError_t attn_bd(const Geo& g, const Ws& w, unsigned long long* clk, hipStream_t s) {
   using C = AttnCfg<B, D>;
   const unsigned grid = (unsigned)(kXcds * xcd_stride(g.bh, g.Nb));
   if (g.fp4_format == DAP_FP4_NVFP4)
-    attn_kernel<B, D, true><<<grid, C::NT, 0, s>>>(g, w);
+    attn_kernel<B, D, true, kClk><<<grid, C::NT, 0, s>>>(g, w, clk);
   else
-    attn_kernel<B, D, false><<<grid, C::NT, 0, s>>>(g, w);
+    attn_kernel<B, D, false, kClk><<<grid, C::NT, 0, s>>>(g, w, clk);
   return hipGetLastError();
+}
+
+template <bool kClk>
+hipError_t attn_any(const Geo& g, const Ws& w, unsigned long long* clk, hipStream_t s) {
+  if (g.D == 64) {
+    if (g.B == 16) return attn_bd<16, 64, kClk>(g, w, clk, s);
+    if (g.B == 64) return attn_bd<64, 64, kClk>(g, w, clk, s);
+    return attn_bd<128, 64, kClk>(g, w, clk, s);
+  }
+  if (g.B == 16) return attn_bd<16, 128, kClk>(g, w, clk, s);
+  if (g.B == 64) return attn_bd<64, 128, kClk>(g, w, clk, s);
+  return attn_bd<128, 128, kClk>(g, w, clk, s);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Geo& g, const Ws& w, hipStream_t s) {
-  if (g.D == 64) {
-    if (g.B == 16) return attn_bd<16, 64>(g, w, s);
-    if (g.B == 64) return attn_bd<64, 64>(g, w, s);
-    return attn_bd<128, 64>(g, w, s);
-  }
-  if (g.B == 16) return attn_bd<16, 128>(g, w, s);
-  if (g.B == 64) return attn_bd<64, 128>(g, w, s);
-  return attn_bd<128, 128>(g, w, s);
+  return attn_any<false>(g, w, nullptr, s);
+}
+
+hipError_t launch_attention_clocked(const Geo& g, const Ws& w, unsigned long long* clk, hipStream_t s) {
+  return attn_any<true>(g, w, clk, s);
 }
 
 }  // namespace dap

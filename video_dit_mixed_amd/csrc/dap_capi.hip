@@ -302,6 +302,20 @@ dap_status dap_attention(const dap_config* cfg, void* ws, size_t ws_bytes, hipSt
   return hip_status(e);
 }
 
+dap_status dap_attention_section_clocks(const dap_config* cfg, void* ws, size_t ws_bytes,
+                                        uint64_t* clocks, hipStream_t stream) {
+  Geo g;
+  dap_layout L;
+  dap_status st = check_call(cfg, ws, ws_bytes, &g, &L);
+  if (st != DAP_OK) return st;
+  if (!clocks || (reinterpret_cast<uintptr_t>(clocks) & 7) != 0) return DAP_E_INVALID;
+  const Ws w = make_ws(ws, L);
+  hipError_t e = dap::launch_attention_clocked(g, w, reinterpret_cast<unsigned long long*>(clocks), stream);
+  if (e == hipSuccess)
+    e = dap::launch_stage(g, w, dap::kAcceptAttention, DAP_STAGE_ATTENDED, stream);
+  return hip_status(e);
+}
+
 dap_status dap_restore(const dap_config* cfg, const void* ws, size_t ws_bytes, void* out,
                        hipStream_t stream) {
   Geo g;

@@ -128,6 +128,9 @@ hipError_t launch_prepare(const Geo& g, const uint16_t* q, const uint16_t* k, co
 hipError_t launch_draft(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_rank(const Geo& g, const Ws& w, hipStream_t s);
 hipError_t launch_attention(const Geo& g, const Ws& w, hipStream_t s);
+// the same attention, summing shader-clock cycles per part of the key-block loop into clk
+// (4 phases x 8 counters, see dap_attention_section_clocks)
+hipError_t launch_attention_clocked(const Geo& g, const Ws& w, unsigned long long* clk, hipStream_t s);
 hipError_t launch_restore(const Geo& g, const Ws& w, uint16_t* out, hipStream_t s);
 hipError_t launch_stage(const Geo& g, const Ws& w, uint32_t accept, uint32_t next, hipStream_t s);
 
