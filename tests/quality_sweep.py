@@ -3,7 +3,7 @@
     python tests/quality_sweep.py --leg gpu [--workload hunyuan720p_33x45x80] [--out FILE]
     python tests/quality_sweep.py --leg cpu [--out FILE]
 
-The pages judge a precision allocation by the relative L2 error of the attention output against
+The pages rate a precision allocation by the relative L2 error of the attention output against
 full attention at a similar latency, and compare single-precision sparse allocations with 4/8-bit
 mixes and the average-only draft with the average/max mix (pchao.org blog on DraftAttention2,
 Figure 1 caption, panel (b); the section 关键结果与论文证据, items on Figure 1(b) and on Table 3 /
