@@ -3,8 +3,9 @@
 // The attention kernel's products (S^T = K Q^T and O^T += V^T P^T) take the tile operand (K rows,
 // V^T rows) from LDS, one 16-byte read per lane -- 1 KB per wave -- per 32x32x16 bf16 product,
 // and the query-side operand from registers.  This program times that pattern in isolation: one
-// 512-thread workgroup per compute unit (two waves per SIMD, as in the attention kernel), each
-// wave looping over products and/or LDS reads, cycles taken with s_memtime (shader clock).
+// workgroup per compute unit, of 512 threads (two waves per SIMD, as in the attention kernel) and
+// then of 256 (one wave per SIMD, the occupancy a wave of 64 queries would need for its registers),
+// each wave looping over products and/or LDS reads, cycles taken with s_memtime (shader clock).
 //
 //   registers            products only, A from registers: the matrix-core peak (32 cycles each)
 //   lds_per_product      each product reads its A operand from LDS, scheduled by the compiler
@@ -48,7 +49,7 @@ template <int P>
 __global__ __launch_bounds__(kThreads) void feed_kernel(unsigned long long* cycles, float* sink, int iters) {
   __shared__ uint4 lds[kSlots];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kSlots; i += kThreads) lds[i] = make_uint4(3u * i, 5u * i + 1, 7u * i + 2, 0x3f803f80u);
+  for (int i = tid; i < kSlots; i += (int)blockDim.x) lds[i] = make_uint4(3u * i, 5u * i + 1, 7u * i + 2, 0x3f803f80u);
   __syncthreads();
   const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
   const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(0x3f813f81u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(kThreads) void feed_kernel(unsigned long long* cycl
 }
 
 template <int P>
-hipError_t launch(int grid, unsigned long long* cycles, float* sink, int iters) {
-  feed_kernel<P><<<grid, kThreads>>>(cycles, sink, iters);
+hipError_t launch(int grid, int threads, unsigned long long* cycles, float* sink, int iters) {
+  feed_kernel<P><<<grid, threads>>>(cycles, sink, iters);
   return hipGetLastError();
 }
 
@@ -118,14 +119,16 @@ int main(int argc, char** argv) {
     return 1;
   }
   unsigned long long* h = new unsigned long long[grid];
+  for (int wps = 2; wps >= 1; --wps) {  // waves per SIMD
+  const int threads = 256 * wps;      // four SIMDs per compute unit
   for (int p = 0; p < kPatterns; ++p) {
     for (int rep = 0; rep < 2; ++rep) {  // the first run warms the clocks up
-      hipError_t e = p == kRegisters       ? launch<kRegisters>(grid, d_cycles, d_sink, iters)
-                     : p == kLdsPerProduct ? launch<kLdsPerProduct>(grid, d_cycles, d_sink, iters)
-                     : p == kLdsB          ? launch<kLdsB>(grid, d_cycles, d_sink, iters)
-                     : p == kLdsPerTwo     ? launch<kLdsPerTwo>(grid, d_cycles, d_sink, iters)
-                     : p == kLdsSoftmaxValu ? launch<kLdsSoftmaxValu>(grid, d_cycles, d_sink, iters)
-                                           : launch<kLdsOnly>(grid, d_cycles, d_sink, iters);
+      hipError_t e = p == kRegisters       ? launch<kRegisters>(grid, threads, d_cycles, d_sink, iters)
+                     : p == kLdsPerProduct ? launch<kLdsPerProduct>(grid, threads, d_cycles, d_sink, iters)
+                     : p == kLdsB          ? launch<kLdsB>(grid, threads, d_cycles, d_sink, iters)
+                     : p == kLdsPerTwo     ? launch<kLdsPerTwo>(grid, threads, d_cycles, d_sink, iters)
+                     : p == kLdsSoftmaxValu ? launch<kLdsSoftmaxValu>(grid, threads, d_cycles, d_sink, iters)
+                                           : launch<kLdsOnly>(grid, threads, d_cycles, d_sink, iters);
       if (e == hipSuccess) e = hipDeviceSynchronize();
       if (e != hipSuccess) {
         std::fprintf(stderr, "%s: %s\n", kNames[p], hipGetErrorString(e));
@@ -136,16 +139,17 @@ int main(int argc, char** argv) {
     double avg = 0;
     for (int i = 0; i < grid; ++i) avg += (double)h[i];
     avg /= grid;
-    // per SIMD: two waves, kUnroll reads or products per wave and iteration (two products per
-    // read in lds_per_two_products); per compute unit: eight waves of 1 KB reads
-    const double units = 2.0 * iters * kUnroll * (p == kLdsPerTwo ? 2 : 1);
-    const double lds_bytes = p == kRegisters ? 0.0 : 8.0 * iters * kUnroll * 1024;
+    // per SIMD: wps waves, kUnroll reads or products per wave and iteration (two products per
+    // read in lds_per_two_products); per compute unit: 4 wps waves of 1 KB reads
+    const double units = (double)wps * iters * kUnroll * (p == kLdsPerTwo ? 2 : 1);
+    const double lds_bytes = p == kRegisters ? 0.0 : 4.0 * wps * iters * kUnroll * 1024;
     const double per = avg / units;
     char frac[32] = "null";  // a 32x32x16 bf16 product takes 32 cycles at the peak
     if (p != kLdsOnly) std::snprintf(frac, sizeof(frac), "%.3f", 32.0 / per);
-    std::printf("{\"pattern\": \"%s\", \"cycles\": %.0f, \"cycles_per_%s_per_simd\": %.2f, "
+    std::printf("{\"pattern\": \"%s\", \"waves_per_simd\": %d, \"cycles\": %.0f, \"cycles_per_%s_per_simd\": %.2f, "
                 "\"matrix_core_fraction\": %s, \"lds_bytes_per_clk_per_cu\": %.1f, \"cus\": %d}\n",
-                kNames[p], avg, p == kLdsOnly ? "read" : "product", per, frac, lds_bytes / avg, cus);
+                kNames[p], wps, avg, p == kLdsOnly ? "read" : "product", per, frac, lds_bytes / avg, cus);
+  }
   }
   delete[] h;
   hipFree(d_cycles);
