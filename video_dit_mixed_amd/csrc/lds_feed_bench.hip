@@ -152,7 +152,6 @@ int main(int argc, char** argv) {
   }
   }
   delete[] h;
-  hipFree(d_cycles);
-  hipFree(d_sink);
-  return 0;
+  const bool freed = hipFree(d_cycles) == hipSuccess && hipFree(d_sink) == hipSuccess;
+  return freed ? 0 : 1;
 }
